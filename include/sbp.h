@@ -1,0 +1,261 @@
+/*
+ * sbp.h -- one data-parallel rank's gradient-sync and sharded-optimizer hot
+ * path on an AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The path, per optimizer step:
+ *   1. bucket plan      per-parameter offsets in flat gradient buckets, each
+ *                       bucket split into N equal chunks, one per rank
+ *   2. pack             per-tensor bf16 gradients copied into the buckets
+ *   3. reduce           this rank's reduce-scatter share: R peer bf16 chunks
+ *                       summed in fp32 in ascending rank order
+ *   4. normalise        one fp32 multiply by 1/(R*K) or 1/global_token_count
+ *   5. accumulate       fp32 accumulation over microbatches
+ *   6. AdamW + emit     mixed-precision AdamW on the owned shard (fp32 master,
+ *                       m, v) and the updated bf16 parameter shard written
+ *                       out for the all-gather
+ * Steps 3-6 of the last microbatch run as one fused streaming kernel.
+ *
+ * Sources (public pages on data-parallel training):
+ *   "Parallelisms" (vladislavkruglikov.com/articles/parallelisms), sections
+ *     Data parallel, Gradient bucketing, ZeRO-1, ZeRO-2, ZeRO-3, FSDP /
+ *     Flat parameter;
+ *   "Distributed Training and Parallelism" (naatyu.github.io/atlas/training/
+ *     parallelism), sections "Data parallelism and the global gradient",
+ *     "ZeRO and sharded state";
+ *   "Parallelism Starts With the Bottleneck" (rajdeepmondal.com), sections
+ *     "Allreduce equals reducescatter plus allgather", "Data parallelism is
+ *     simple and pays for it in memory", "ZeRO removes the copies without
+ *     adding bandwidth".
+ *
+ * Conventions for every call below:
+ *   - Return value: SBP_OK or a negative status; sbp_last_error() then holds
+ *     a message for the calling thread.  Invalid arguments are reported
+ *     before anything is enqueued; nothing is written on error.
+ *   - n == 0 (after the count and hyperparameter checks) returns SBP_OK
+ *     without reading any pointer or launching anything.
+ *   - Device pointers are caller-owned device (HBM) memory.  No call
+ *     allocates or frees device memory.  Host arrays are read during the
+ *     call only.
+ *   - Device calls validate on the host, enqueue on `stream` and return;
+ *     a fault in a kernel surfaces at the caller's next synchronisation.
+ *   - bf16 values are passed as their 16-bit patterns (uint16 storage).
+ *   - Arithmetic is IEEE binary32 with one round-to-nearest-even rounding per
+ *     operation (no fused multiply-add), subnormals kept; a sum over peers
+ *     starts from peer 0's value and adds peers 1..R-1 in that order.  Results
+ *     are therefore fully determined by the inputs.
+ */
+#ifndef SBP_H
+#define SBP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sbp_status;
+#define SBP_OK 0
+#define SBP_EINVAL (-1) /* bad argument: null pointer, bad size/count/index  */
+#define SBP_EALIGN (-2) /* a pointer lacks the alignment the call requires   */
+#define SBP_ERANGE (-3) /* a size overflows int64 or a documented maximum    */
+#define SBP_EHIP (-4)   /* the HIP runtime refused a launch                  */
+#define SBP_ENOMEM (-5) /* host allocation failed                            */
+
+#define SBP_MAX_PEERS 16 /* largest R accepted by the reduce-type calls */
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* sbp_last_error(void);
+/* Library version string. */
+const char* sbp_version(void);
+
+/* ------------------------------------------------------------------------
+ * Bucket plan (host only).
+ *
+ * "Parallelisms", Gradient bucketing: gradients are collected into buffers
+ * that are communicated once ready; Data parallel: buckets for later layers
+ * are ready first during backward; FSDP / Flat parameter: a bucket is one
+ * contiguous buffer that concatenates parameters; ZeRO-2: each ready bucket
+ * is reduce-scattered and each rank keeps the 1/N shard it owns.
+ *
+ * Rule (readings where the pages are silent):
+ *   - tensors are visited in reverse registration order (SBP_ORDER_REVERSE,
+ *     the default) or in registration order (SBP_ORDER_FORWARD);
+ *   - a tensor is added to the open bucket at the first multiple of
+ *     align_elems at or after the bucket's used length (the first tensor at
+ *     0); the bucket closes once 2*used >= bucket_cap_bytes (the cap counts
+ *     bf16 gradient bytes); tensors are never split, so a bucket may exceed
+ *     the cap by its last tensor and a tensor larger than the cap forms its
+ *     own bucket; the last open bucket closes at the end;
+ *   - each bucket is zero-padded to a multiple of align_elems * world_n
+ *     elements and split into world_n equal chunks; rank s owns chunk s of
+ *     every bucket, and its shard is those chunks in bucket order.
+ *
+ * numel[n_tensors]   element counts in registration order (>= 0 each)
+ * bucket_cap_bytes   > 0
+ * world_n            shard divisor N, > 0
+ * align_elems        power of two, 1..4096 (8 keeps every chunk 16-B aligned)
+ * flags              SBP_ORDER_REVERSE (0) or SBP_ORDER_FORWARD
+ * out                receives an immutable plan; free with sbp_plan_free.
+ *                    A plan is read-only after creation and may be shared
+ *                    between threads.
+ * Errors: SBP_EINVAL (null, n_tensors < 0, negative numel, bad cap/N/align/
+ * flags), SBP_ERANGE (a sum overflows int64), SBP_ENOMEM.
+ * ---------------------------------------------------------------------- */
+typedef struct sbp_plan sbp_plan;
+
+#define SBP_ORDER_REVERSE 0u
+#define SBP_ORDER_FORWARD 1u
+
+sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
+                           int64_t bucket_cap_bytes, int32_t world_n,
+                           int32_t align_elems, uint32_t flags,
+                           sbp_plan** out);
+void sbp_plan_free(sbp_plan* plan);
+
+/* Plan queries.  Counts and offsets are in elements. */
+int32_t sbp_plan_num_tensors(const sbp_plan* plan);
+int32_t sbp_plan_num_buckets(const sbp_plan* plan);
+int32_t sbp_plan_world_n(const sbp_plan* plan);
+/* Elements of one rank's shard (the same for every rank). */
+int64_t sbp_plan_shard_numel(const sbp_plan* plan);
+/* Elements of the flat buffer holding all buckets (= N * shard numel). */
+int64_t sbp_plan_flat_numel(const sbp_plan* plan);
+/* Tensor t's bucket and its offset inside the bucket. */
+sbp_status sbp_plan_tensor(const sbp_plan* plan, int32_t t, int32_t* bucket,
+                           int64_t* offset);
+/* Bucket b: used length, padded length, chunk (= padded / N), start of its
+ * chunk in a rank's shard, start of the bucket in the flat buffer.  Any of
+ * the output pointers may be null. */
+sbp_status sbp_plan_bucket(const sbp_plan* plan, int32_t b, int64_t* used,
+                           int64_t* padded, int64_t* chunk,
+                           int64_t* shard_offset, int64_t* flat_offset);
+/* Tensor ids of bucket b in the order they were placed; writes up to `cap`
+ * ids and returns the bucket's tensor count in *count. */
+sbp_status sbp_plan_bucket_tensors(const sbp_plan* plan, int32_t b,
+                                   int32_t* ids, int32_t cap, int32_t* count);
+/* Persistent model-state bytes per rank: bf16 params (2) + bf16 grads (2) +
+ * fp32 master, m, v (12) per parameter, with stage 0 = plain DP (all
+ * replicated), 1 = optimizer state sharded, 2 = + gradients, 3 = + params
+ * ("Parallelism Strategies in Distributed Computing", Cost per strategy and
+ * ZeRO and FSDP; "Parallelism Starts With the Bottleneck", memory section).
+ * Counted over the padded flat buffer; activations and temporary buckets
+ * are excluded.  Errors: SBP_EINVAL (null, stage outside 0..3). */
+sbp_status sbp_plan_state_bytes(const sbp_plan* plan, int32_t zero_stage,
+                                int64_t* per_rank_bytes);
+
+/* ------------------------------------------------------------------------
+ * Normalisation factors ("Distributed Training and Parallelism", Data
+ * parallelism and the global gradient: average over R ranks, or scale by
+ * R / global valid-token count; with the 1/R average that is 1/C).
+ * Computed in float64 and rounded once to binary32.
+ * ---------------------------------------------------------------------- */
+/* *scale = fl32(1 / (R * K)).  Errors: SBP_EINVAL (null, R < 1, K < 1). */
+sbp_status sbp_mean_scale(int32_t R, int32_t K, float* scale);
+/* *scale = fl32(1 / sum(counts[0..R-1])).  Errors: SBP_EINVAL (null, R < 1,
+ * a negative count, a zero total), SBP_ERANGE (the total overflows). */
+sbp_status sbp_tokens_scale(const int64_t* counts, int32_t R, float* scale);
+
+/* ------------------------------------------------------------------------
+ * Pack ("Parallelisms", Gradient bucketing and FSDP: gradients gathered
+ * into flat communication buffers at fixed offsets).
+ *
+ * Copies every tensor of bucket `bucket` (or of all buckets if bucket == -1)
+ * bit for bit from tensor_grads[t] to flat[flat_offset_b + offset_t ...],
+ * and writes +0 (0x0000) into every other element of those buckets.
+ *
+ * tensor_grads  host array of plan->n_tensors device pointers to bf16
+ *               gradients (2-byte aligned); entries of tensors outside the
+ *               selected bucket(s) are not read and may be null.  Sources
+ *               that are 16-byte aligned take the vector path.
+ * flat          device bf16 buffer of sbp_plan_flat_numel elements,
+ *               16-byte aligned; must not overlap any source.
+ * Errors: SBP_EINVAL (null plan/array/buffer, null source of a selected
+ * tensor, bucket out of range), SBP_EALIGN (flat not 16-B aligned, a source
+ * not 2-B aligned), SBP_EHIP.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
+                          const void* const* tensor_grads, void* flat,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Reduce ("Parallelisms", ZeRO-1: reduce-scatter leaves each worker the
+ * reduced gradient shard of the parameters it owns; "Distributed Training
+ * and Parallelism": the reduction order changes the bits, so it is fixed).
+ *
+ * out[i] = fl( S[i] * scale ),  S[i] = fp32(p0[i]) + fp32(p1[i]) + ... in
+ * ascending peer order, one rounding per addition.
+ *
+ * peers  host array of R device pointers to bf16 chunks of n elements
+ * R      1..SBP_MAX_PEERS
+ * out    device fp32[n]
+ * All device pointers 16-byte aligned; out must not overlap a peer.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n,
+                            float scale, float* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Accumulate ("Distributed Training and Parallelism": intermediate
+ * reductions suppressed over microbatches, the last pass synchronises;
+ * "Parallelisms", ZeRO-2: accumulation adds later microbatches' shards).
+ *
+ * acc[i] = S[i] if first != 0, else fl(acc[i] + S[i]); S as in reduce, no
+ * scaling (the scale is applied once, in the fused step).  R = 1 is a
+ * rank's local (no_sync) accumulation; R > 1 accumulates reduce-scattered
+ * shards.  acc is read and written in place.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_accumulate_grads(float* acc, const void* const* peers,
+                                int32_t R, int64_t n, int32_t first,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fused shard step: reduce + normalise + AdamW + bf16 emit, one pass.
+ *
+ * ("Parallelisms", ZeRO-1: each worker updates its owned shard with its
+ * local optimizer state -- first and second moments, a step counter and an
+ * fp32 master copy -- then the updated shards are all-gathered; ZeRO-3: the
+ * same update on a persistent 1/N shard.)
+ *
+ * Per element i:
+ *   G = acc[i] + S[i]   (acc given, R >= 1)   S = ascending peer sum
+ *   G = S[i]            (acc null)
+ *   G = acc[i]          (R == 0)
+ *   g = fl(G * scale)
+ *   m'  = b1*m + (1-b1)*g
+ *   v'  = b2*v + (1-b2)*(g*g)
+ *   d   = sqrt(v')*c2 + eps                  (sqrt correctly rounded)
+ *   th' = th*decay - step_size*(m'/d)        (divide correctly rounded)
+ *   master[i] = th', m[i] = m', v[i] = v', param_out[i] = bf16_rne(th')
+ * with, per call, from the binary32 hyperparameters in float64, each rounded
+ * once to binary32: bc1 = 1 - b1^t, bc2 = 1 - b2^t (powers by repeated
+ * multiplication), step_size = lr/bc1, c2 = 1/sqrt(bc2), decay = 1 - lr*wd,
+ * 1-b1 and 1-b2.  bf16_rne: nearest, ties to even; NaN stays NaN (sign
+ * kept, quiet bit set); overflow to +-inf.
+ *
+ * peers      host array of R device bf16 pointers (unused if R == 0)
+ * R          0..SBP_MAX_PEERS; 0 requires acc
+ * acc        device fp32[n] or null
+ * master,m,v device fp32[n], updated in place
+ * param_out  device bf16[n] (the all-gather send buffer)
+ * hp         hyperparameters; hp->step = t >= 1 (1-based, once per
+ *            optimizer step, not per microbatch)
+ * All device pointers 16-byte aligned and pairwise non-overlapping.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} sbp_adamw_hparams;
+
+sbp_status sbp_adamw_shard(const void* const* peers, int32_t R,
+                           const float* acc, float scale, float* master,
+                           float* m, float* v, void* param_out, int64_t n,
+                           const sbp_adamw_hparams* hp, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBP_H */

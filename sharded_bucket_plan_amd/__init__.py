@@ -1,0 +1,291 @@
+"""Python binding of libsbp.so, the shard-step C ABI (include/sbp.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Device buffers are torch tensors on a ROCm device (PyTorch supplies
+device memory and streams); they are passed as raw pointers together with
+the current HIP stream.  There is no fallback: if libsbp.so is missing, or a
+call fails, an error is raised.
+
+Functions (same names as the C calls without the "sbp_" prefix):
+  bucket_plan, pack_grads, reduce_shard, accumulate_grads, adamw_shard,
+  mean_scale, tokens_scale.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsbp.so")
+
+SBP_OK, SBP_EINVAL, SBP_EALIGN, SBP_ERANGE, SBP_EHIP, SBP_ENOMEM = 0, -1, -2, -3, -4, -5
+SBP_MAX_PEERS = 16
+ORDER_REVERSE, ORDER_FORWARD = 0, 1
+
+# every function include/sbp.h declares
+EXPORTS = (
+    "sbp_last_error", "sbp_version", "sbp_bucket_plan", "sbp_plan_free",
+    "sbp_plan_num_tensors", "sbp_plan_num_buckets", "sbp_plan_world_n",
+    "sbp_plan_shard_numel", "sbp_plan_flat_numel", "sbp_plan_tensor", "sbp_plan_bucket",
+    "sbp_plan_bucket_tensors", "sbp_plan_state_bytes", "sbp_mean_scale", "sbp_tokens_scale",
+    "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
+)
+
+
+class SbpError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"sbp status {status}: {message}")
+        self.status = status
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int64)]
+
+
+_lib = None
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def lib():
+    """The loaded C library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int32
+    sig = {
+        "sbp_last_error": ([], ctypes.c_char_p),
+        "sbp_version": ([], ctypes.c_char_p),
+        "sbp_bucket_plan": ([_i64p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                             ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)], st),
+        "sbp_plan_free": ([ctypes.c_void_p], None),
+        "sbp_plan_num_tensors": ([ctypes.c_void_p], ctypes.c_int32),
+        "sbp_plan_num_buckets": ([ctypes.c_void_p], ctypes.c_int32),
+        "sbp_plan_world_n": ([ctypes.c_void_p], ctypes.c_int32),
+        "sbp_plan_shard_numel": ([ctypes.c_void_p], ctypes.c_int64),
+        "sbp_plan_flat_numel": ([ctypes.c_void_p], ctypes.c_int64),
+        "sbp_plan_tensor": ([ctypes.c_void_p, ctypes.c_int32, _i32p, _i64p], st),
+        "sbp_plan_bucket": ([ctypes.c_void_p, ctypes.c_int32] + [_i64p] * 5, st),
+        "sbp_plan_bucket_tensors": ([ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                     _i32p], st),
+        "sbp_plan_state_bytes": ([ctypes.c_void_p, ctypes.c_int32, _i64p], st),
+        "sbp_mean_scale": ([ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)], st),
+        "sbp_tokens_scale": ([_i64p, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)], st),
+        "sbp_pack_grads": ([ctypes.c_void_p, ctypes.c_int32, _vpp, ctypes.c_void_p,
+                            ctypes.c_void_p], st),
+        "sbp_reduce_shard": ([_vpp, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_void_p, ctypes.c_void_p], st),
+        "sbp_accumulate_grads": ([ctypes.c_void_p, _vpp, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_void_p], st),
+        "sbp_adamw_shard": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_int64, ctypes.POINTER(AdamWHParams), ctypes.c_void_p], st),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != SBP_OK:
+        raise SbpError(status, lib().sbp_last_error().decode())
+
+
+def version():
+    return lib().sbp_version().decode()
+
+
+# ---- plan ------------------------------------------------------------------
+
+class Plan:
+    """An immutable bucket plan (owns the C handle)."""
+
+    def __init__(self, handle, numels):
+        self._h = ctypes.c_void_p(handle)
+        self.numels = [int(x) for x in numels]
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None and self._h.value:
+            _lib.sbp_plan_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def num_tensors(self):
+        return lib().sbp_plan_num_tensors(self._h)
+
+    @property
+    def num_buckets(self):
+        return lib().sbp_plan_num_buckets(self._h)
+
+    @property
+    def world_n(self):
+        return lib().sbp_plan_world_n(self._h)
+
+    @property
+    def shard_numel(self):
+        return lib().sbp_plan_shard_numel(self._h)
+
+    @property
+    def flat_numel(self):
+        return lib().sbp_plan_flat_numel(self._h)
+
+    def tensor(self, t):
+        b, o = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().sbp_plan_tensor(self._h, t, ctypes.byref(b), ctypes.byref(o)))
+        return b.value, o.value
+
+    def bucket(self, b):
+        vals = [ctypes.c_int64() for _ in range(5)]
+        _check(lib().sbp_plan_bucket(self._h, b, *[ctypes.byref(v) for v in vals]))
+        return dict(zip(("used", "padded", "chunk", "shard_offset", "flat_offset"),
+                        (v.value for v in vals)))
+
+    def bucket_tensors(self, b):
+        cnt = ctypes.c_int32()
+        _check(lib().sbp_plan_bucket_tensors(self._h, b, None, 0, ctypes.byref(cnt)))
+        ids = (ctypes.c_int32 * max(cnt.value, 1))()
+        _check(lib().sbp_plan_bucket_tensors(self._h, b, ids, cnt.value, ctypes.byref(cnt)))
+        return list(ids[:cnt.value])
+
+    def state_bytes(self, zero_stage):
+        out = ctypes.c_int64()
+        _check(lib().sbp_plan_state_bytes(self._h, zero_stage, ctypes.byref(out)))
+        return out.value
+
+
+def bucket_plan(numels, bucket_cap_bytes, world_n, align=8, order="reverse"):
+    """sbp_bucket_plan: flat-bucket layout of a parameter list (host only)."""
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
+    h = ctypes.c_void_p()
+    flags = ORDER_REVERSE if order == "reverse" else ORDER_FORWARD
+    if order not in ("reverse", "forward"):
+        flags = 0xFF  # rejected by the library
+    _check(lib().sbp_bucket_plan(arr, len(numels), int(bucket_cap_bytes), int(world_n),
+                                 int(align), flags, ctypes.byref(h)))
+    return Plan(h.value, numels)
+
+
+def mean_scale(R, K=1):
+    out = ctypes.c_float()
+    _check(lib().sbp_mean_scale(int(R), int(K), ctypes.byref(out)))
+    return out.value
+
+
+def tokens_scale(counts):
+    arr = (ctypes.c_int64 * max(len(counts), 1))(*[int(c) for c in counts])
+    out = ctypes.c_float()
+    _check(lib().sbp_tokens_scale(arr, len(counts), ctypes.byref(out)))
+    return out.value
+
+
+# ---- device calls ------------------------------------------------------------
+
+def _stream(stream, tensor):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(tensor.device).cuda_stream)
+
+
+def _dev(t, itemsize, what):
+    if not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if t.element_size() != itemsize:
+        raise ValueError(f"{what}: expected {itemsize}-byte elements, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _f32(t, what):
+    import torch
+    if t.dtype != torch.float32:
+        raise ValueError(f"{what}: expected float32, got {t.dtype}")
+    return _dev(t, 4, what)
+
+
+def _ptrs(tensors, what):
+    return (ctypes.c_void_p * max(len(tensors), 1))(*[_dev(t, 2, what) for t in tensors])
+
+
+def pack_grads(plan, grads, flat, bucket=-1, stream=None):
+    """sbp_pack_grads: copy per-tensor bf16 grads into the flat buckets (+0 elsewhere).
+
+    grads: one 2-byte device tensor per plan tensor (None allowed for tensors
+    outside the selected bucket); flat: 2-byte device tensor of plan.flat_numel.
+    """
+    if len(grads) != plan.num_tensors:
+        raise ValueError("pack_grads: one gradient per plan tensor")
+    if flat.numel() != plan.flat_numel:
+        raise ValueError("pack_grads: flat has the wrong size")
+    arr = (ctypes.c_void_p * max(len(grads), 1))()
+    for t, g in enumerate(grads):
+        if g is None:
+            continue
+        if g.numel() != plan.numels[t]:
+            raise ValueError(f"pack_grads: tensor {t} has {g.numel()} elements")
+        arr[t] = g.data_ptr() if g.numel() else None
+        if g.numel():
+            _dev(g, 2, "pack_grads grads")
+    _check(lib().sbp_pack_grads(plan.handle, int(bucket), arr, _dev(flat, 2, "pack_grads flat"),
+                                _stream(stream, flat)))
+
+
+def reduce_shard(peers, scale, out, stream=None):
+    """sbp_reduce_shard: out = (ascending fp32 sum of the bf16 peers) * scale."""
+    n = out.numel()
+    if any(p.numel() != n for p in peers):
+        raise ValueError("reduce_shard: peers and out differ in size")
+    _check(lib().sbp_reduce_shard(_ptrs(peers, "reduce_shard peers"), len(peers), n,
+                                  float(scale), _f32(out, "reduce_shard out"),
+                                  _stream(stream, out)))
+
+
+def accumulate_grads(acc, peers, first, stream=None):
+    """sbp_accumulate_grads: acc = S (first) or acc + S."""
+    n = acc.numel()
+    if any(p.numel() != n for p in peers):
+        raise ValueError("accumulate_grads: peers and acc differ in size")
+    _check(lib().sbp_accumulate_grads(_f32(acc, "accumulate_grads acc"),
+                                      _ptrs(peers, "accumulate_grads peers"), len(peers), n,
+                                      1 if first else 0, _stream(stream, acc)))
+
+
+@dataclass
+class AdamW:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+
+def adamw_shard(peers, acc, scale, master, m, v, param_out, hp, step, stream=None):
+    """sbp_adamw_shard: fused reduce (+acc) -> *scale -> AdamW -> bf16 emit."""
+    n = master.numel()
+    for t, what in ((m, "m"), (v, "v"), (param_out, "param_out")):
+        if t.numel() != n:
+            raise ValueError(f"adamw_shard: {what} has the wrong size")
+    if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
+        raise ValueError("adamw_shard: peers/acc differ in size")
+    h = AdamWHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, int(step))
+    _check(lib().sbp_adamw_shard(
+        _ptrs(peers, "adamw_shard peers"), len(peers),
+        None if acc is None else _f32(acc, "adamw_shard acc"), float(scale),
+        _f32(master, "adamw_shard master"), _f32(m, "adamw_shard m"), _f32(v, "adamw_shard v"),
+        _dev(param_out, 2, "adamw_shard param_out"), n, ctypes.byref(h),
+        _stream(stream, master)))

@@ -1,0 +1,126 @@
+"""Shared helpers of the GPU tests: device buffers, seeded inputs on both
+sides, ordered-bit ulp distances, guard bands."""
+
+import numpy as np
+import pytest
+
+import synth
+
+
+def need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this process")
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def empty_u16(n, guard=0):
+    """2-byte device tensor (int16 storage for bf16 bits)."""
+    import torch
+    return torch.empty(n + 2 * guard, dtype=torch.int16, device=dev())
+
+
+def to_np_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def to_np_f32(t):
+    return t.cpu().numpy()
+
+
+def from_np_u16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev())
+
+
+def from_np_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+# ---- ulp distances on ordered bit patterns ------------------------------------
+
+def _ordered32(a):
+    i = np.ascontiguousarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    return np.where(i < 0, -(i & 0x7FFFFFFF), i)
+
+
+def ulp_f32(a, b):
+    """Distance in binary32 ulps (+0 and -0 coincide; two NaNs are 0 apart,
+    a NaN against a number is infinitely far)."""
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    d = np.abs(_ordered32(a) - _ordered32(b)).astype(np.float64)
+    na, nb = np.isnan(a), np.isnan(b)
+    d[na & nb] = 0
+    d[na ^ nb] = np.inf
+    return d
+
+
+def ulp_bf16(a, b):
+    a = np.asarray(a, np.uint16).astype(np.uint32) << 16
+    b = np.asarray(b, np.uint16).astype(np.uint32) << 16
+    return ulp_f32(a.view(np.float32), b.view(np.float32)) / 65536.0
+
+
+def assert_bits_equal(got, want, what):
+    got = np.ascontiguousarray(got)
+    want = np.ascontiguousarray(want)
+    assert got.shape == want.shape, what
+    if got.dtype == np.float32:
+        g, w = got.view(np.uint32), want.view(np.uint32)
+    else:
+        g, w = got, want
+    bad = np.flatnonzero(g != w)
+    assert bad.size == 0, (f"{what}: {bad.size} of {g.size} differ; first at {bad[:5]}: "
+                           f"got {got.ravel()[bad[:5]]} want {want.ravel()[bad[:5]]}")
+
+
+def assert_state_close(got, want, what, f32_ulps=4, bf16_ulps=1):
+    """spec bar: master/m/v within 4 fp32 ulp, params within 1 bf16 ulp.
+    Returns the largest distance seen (expected 0: the path is bit-exact)."""
+    th, m, v, p = got
+    wth, wm, wv, wp = want
+    worst = 0.0
+    for a, b, name in ((th, wth, "master"), (m, wm, "m"), (v, wv, "v")):
+        d = ulp_f32(a, b)
+        mx = float(d.max()) if d.size else 0.0
+        assert mx <= f32_ulps, f"{what}: {name} off by {mx} ulp"
+        worst = max(worst, mx)
+    d = ulp_bf16(p, wp)
+    mx = float(d.max()) if d.size else 0.0
+    assert mx <= bf16_ulps, f"{what}: param off by {mx} bf16 ulp"
+    return max(worst, mx)
+
+
+# ---- seeded inputs on both sides --------------------------------------------
+
+def host_peers(seed, t, k, R, n, sigma, i0=0):
+    return [synth.normal_bf16(seed, synth.peer_stream(t, k, r), n, sigma, i0) for r in range(R)]
+
+
+def dev_peers(seed, t, k, R, n, sigma, bufs=None):
+    out = bufs if bufs is not None else [empty_u16(n) for _ in range(R)]
+    for r in range(R):
+        synth.dev_normal_bf16(out[r], seed, synth.peer_stream(t, k, r), sigma)
+    return out
+
+
+def guarded(n, itemsize, guard=64, fill=0x5A):
+    """A device buffer with `guard` canary bytes on each side; returns
+    (whole buffer as uint8, the inner view of n elements as a typed tensor)."""
+    import torch
+    g = max(guard, 16)
+    whole = torch.full((n * itemsize + 2 * g,), fill, dtype=torch.uint8, device=dev())
+    inner = whole[g:g + n * itemsize]
+    dt = {2: torch.int16, 4: torch.float32}[itemsize]
+    return whole, inner.view(dt), g
+
+
+def canaries_intact(whole, g, fill=0x5A):
+    w = whole.cpu().numpy()
+    return bool(np.all(w[:g] == fill) and np.all(w[-g:] == fill))

@@ -1,0 +1,166 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every function
+include/sbp.h declares, its planner agrees with the oracle's independent
+planner, and bad arguments come back as error codes before any device work
+(no call here reaches the GPU)."""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import sharded_bucket_plan_amd as sbp
+import synth
+from oracle import plan as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sbp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sbp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(sbp.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sbp.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert sbp.version().startswith("sbp ")
+
+
+def _same_plan(numels, cap, N, align=8, order="reverse"):
+    p = sbp.bucket_plan(numels, cap, N, align, order)
+    o = OP.bucket_plan(numels, cap, N, align, order)
+    assert p.num_buckets == len(o.buckets)
+    assert p.shard_numel == o.shard_numel and p.flat_numel == o.flat_numel
+    for b, ob in enumerate(o.buckets):
+        assert p.bucket(b) == dict(used=ob.used, padded=ob.padded, chunk=ob.chunk,
+                                   shard_offset=ob.shard_offset, flat_offset=ob.flat_offset)
+        assert p.bucket_tensors(b) == ob.tensors
+    for t in range(len(numels)):
+        assert p.tensor(t) == (o.tensor_bucket[t], o.tensor_offset[t])
+    for stage in range(4):
+        assert p.state_bytes(stage) == OP.state_bytes(o.flat_numel, o.shard_numel, stage)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_plan_matches_oracle_on_workloads(name):
+    w = synth.WORKLOADS[name]
+    _same_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+
+
+def test_plan_matches_oracle_on_cap_sweep():
+    w = synth.WORKLOADS["gpt_7b5"]
+    for mib in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        _same_plan(w.numels, mib << 20, w.world_n)
+
+
+def test_plan_matches_oracle_random():
+    rng = random.Random(99)
+    for _ in range(400):
+        T = rng.randint(0, 12)
+        numels = [rng.choice([0, 1, 3, 7, 8, 9, 17, 64, 100, 1000]) for _ in range(T)]
+        _same_plan(numels, rng.randint(1, 3000), rng.choice([1, 2, 3, 4, 8, 64]),
+                   rng.choice([1, 2, 4, 8, 16]), rng.choice(["reverse", "forward"]))
+
+
+def test_plan_rejects_bad_arguments():
+    bad = [([8], 0, 1, 8), ([8], 64, 0, 8), ([8], 64, 1, 3), ([8], 64, 1, 8192), ([-1], 64, 1, 8)]
+    for numels, cap, N, align in bad:
+        with pytest.raises(sbp.SbpError) as e:
+            sbp.bucket_plan(numels, cap, N, align)
+        assert e.value.status == sbp.SBP_EINVAL
+    with pytest.raises(sbp.SbpError):
+        sbp.bucket_plan([8], 64, 1, 8, order="sideways")
+    with pytest.raises(sbp.SbpError) as e:
+        sbp.bucket_plan([2 ** 62, 2 ** 62], 64, 1)
+    assert e.value.status == sbp.SBP_ERANGE
+    p = sbp.bucket_plan([8, 8], 64, 1)
+    with pytest.raises(sbp.SbpError):
+        p.tensor(2)
+    with pytest.raises(sbp.SbpError):
+        p.bucket(-1)
+    with pytest.raises(sbp.SbpError):
+        p.state_bytes(4)
+
+
+def test_scales_match_oracle():
+    from oracle import step as OS
+    for R in (1, 2, 3, 7, 8, 64):
+        for K in (1, 3, 4):
+            assert sbp.mean_scale(R, K) == float(OS.mean_scale(R, K))
+    for t in range(1, 30):
+        counts = [synth.tokens(17, t, r) for r in range(8)]
+        assert sbp.tokens_scale(counts) == float(OS.tokens_scale(counts))
+    for bad in ([0], [], [-1, 5]):
+        with pytest.raises(sbp.SbpError):
+            sbp.tokens_scale(bad)
+    with pytest.raises(sbp.SbpError):
+        sbp.mean_scale(0, 1)
+
+
+def _raw(L, name, *args):
+    return getattr(L, name)(*args)
+
+
+def test_device_calls_validate_before_launch():
+    """Null, misaligned, overlapping and out-of-range arguments are rejected on
+    the host; the fake addresses below are never dereferenced."""
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    peers = (V * 2)(0x100000, 0x200000)
+    hp = sbp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    adam = L.sbp_adamw_shard
+    ok_args = dict(peers=peers, R=2, acc=None, scale=0.5, master=V(0x300000), m=V(0x400000),
+                   v=V(0x500000), p=V(0x600000), n=1024, hp=ctypes.byref(hp))
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return adam(a["peers"], a["R"], a["acc"], a["scale"], a["master"], a["m"], a["v"],
+                    a["p"], a["n"], a["hp"], None)
+
+    assert call(R=17) == sbp.SBP_EINVAL
+    assert call(R=-1) == sbp.SBP_EINVAL
+    assert call(R=0) == sbp.SBP_EINVAL  # R == 0 needs acc
+    assert call(R=0, n=0) == sbp.SBP_OK
+    assert call(peers=(V * 2)(0x100000, None)) == sbp.SBP_EINVAL
+    assert call(peers=(V * 2)(0x100008, 0x200000)) == sbp.SBP_EALIGN
+    assert call(master=V(0x300004)) == sbp.SBP_EALIGN
+    assert call(p=V(0x600002)) == sbp.SBP_EALIGN
+    assert call(master=None) == sbp.SBP_EINVAL
+    assert call(n=-1) == sbp.SBP_EINVAL
+    bad_hp = sbp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0)
+    assert call(hp=ctypes.byref(bad_hp)) == sbp.SBP_EINVAL
+    assert call(hp=None) == sbp.SBP_EINVAL
+    assert call(m=V(0x300000 + 1024)) == sbp.SBP_EINVAL  # overlaps master
+    assert call(p=V(0x100000 + 512)) == sbp.SBP_EINVAL  # overlaps a peer
+    assert call(n=0) == sbp.SBP_OK  # nothing to do, nothing launched
+    assert call(n=0, master=None, peers=None) == sbp.SBP_OK
+    assert call(p=V(0x100000 + 512)) == sbp.SBP_EINVAL
+    assert "overlap" in sbp.lib().sbp_last_error().decode()
+
+    red = L.sbp_reduce_shard
+    assert red(peers, 0, 16, 1.0, V(0x300000), None) == sbp.SBP_EINVAL
+    assert red(peers, 2, 16, 1.0, V(0x300004), None) == sbp.SBP_EALIGN
+    assert red(peers, 2, 16, 1.0, V(0x100000), None) == sbp.SBP_EINVAL  # out overlaps peer 0
+    assert red(peers, 2, 0, 1.0, V(0x300000), None) == sbp.SBP_OK
+    acc = L.sbp_accumulate_grads
+    assert acc(None, peers, 2, 16, 1, None) == sbp.SBP_EINVAL
+    assert acc(V(0x300008), peers, 2, 16, 1, None) == sbp.SBP_EALIGN
+    assert acc(V(0x300000), peers, 2, 0, 0, None) == sbp.SBP_OK
+
+    plan = sbp.bucket_plan([10, 20], 1 << 20, 1)
+    grads = (V * 2)(0x100000, 0x200000)
+    pack = L.sbp_pack_grads
+    assert pack(None, -1, grads, V(0x300000), None) == sbp.SBP_EINVAL
+    assert pack(plan.handle, 5, grads, V(0x300000), None) == sbp.SBP_EINVAL
+    assert pack(plan.handle, -1, grads, V(0x300008), None) == sbp.SBP_EALIGN
+    assert pack(plan.handle, -1, (V * 2)(0x100001, 0x200000), V(0x300000), None) == sbp.SBP_EALIGN
+    assert pack(plan.handle, -1, (V * 2)(None, 0x200000), V(0x300000), None) == sbp.SBP_EINVAL
+    assert pack(plan.handle, -1, grads, V(0x100000 + 16), None) == sbp.SBP_EINVAL  # overlap

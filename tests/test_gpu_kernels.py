@@ -1,0 +1,258 @@
+"""GPU parity of each kernel against the oracle, element by element, on the
+same seeded inputs (HIP path called through the C ABI).  Sizes span several
+tiles and grid-stride passes with ragged tails; edge cases cover empty and
+tiny inputs, every peer count, special values and out-of-bounds writes."""
+
+import numpy as np
+import pytest
+
+import sharded_bucket_plan_amd as sbp
+import synth
+from oracle import plan as OP
+from oracle import step as OS
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+HP = sbp.AdamW()
+SIZES = [1, 7, 8, 9, 2047, 256 * 8 * 3 + 5]
+# 16.8M elements make one grid-stride pass of the largest grid; this spans 2+
+BIG = 256 * 32 * 256 * 8 * 2 + 13
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    H.need_gpu()
+    yield
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_device_generator_matches_host():
+    import torch
+    for n, st, sigma in [(12345, synth.peer_stream(3, 1, 7), 1e-3),
+                         (1 << 20, synth.tensor_stream(2, 0, 1, 9), 1e-2)]:
+        d = H.empty_u16(n)
+        synth.dev_normal_bf16(d, 42, st, sigma)
+        H.assert_bits_equal(H.to_np_u16(d), synth.normal_bf16(42, st, n, sigma), "bf16 gen")
+    f = torch.empty(99991, dtype=torch.float32, device=H.dev())
+    synth.dev_normal_f32(f, 42, synth.master_stream(1), 0.02)
+    H.assert_bits_equal(H.to_np_f32(f), synth.normal_f32(42, synth.master_stream(1), 99991, 0.02),
+                        "f32 gen")
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("n", SIZES)
+def test_reduce_shard(R, n):
+    import torch
+    peers = H.dev_peers(11, 1, 0, R, n, 1e-3)
+    scale = sbp.mean_scale(R)
+    whole, out, g = H.guarded(n, 4)
+    sbp.reduce_shard(peers, scale, out)
+    torch.cuda.synchronize()
+    want = OS.normalise(OS.reduce_peers(H.host_peers(11, 1, 0, R, n, 1e-3)), OS.mean_scale(R))
+    H.assert_bits_equal(H.to_np_f32(out), want, f"reduce R={R} n={n}")
+    assert H.canaries_intact(whole, g)
+
+
+def test_reduce_shard_big_multi_pass():
+    import torch
+    R, n = 8, BIG
+    peers = H.dev_peers(12, 1, 0, R, n, 1e-3)
+    out = torch.empty(n, dtype=torch.float32, device=H.dev())
+    sbp.reduce_shard(peers, 0.125, out)
+    torch.cuda.synchronize()
+    want = OS.normalise(OS.reduce_peers(H.host_peers(12, 1, 0, R, n, 1e-3)), np.float32(0.125))
+    H.assert_bits_equal(H.to_np_f32(out), want, "reduce big")
+
+
+@pytest.mark.parametrize("R", [1, 3, 8])
+@pytest.mark.parametrize("n", [1, 9, 256 * 8 * 3 + 5, BIG])
+def test_accumulate_grads(R, n):
+    import torch
+    K = 3
+    acc = torch.empty(n, dtype=torch.float32, device=H.dev())
+    bufs = None
+    A = None
+    for k in range(K):
+        bufs = H.dev_peers(13, 2, k, R, n, 1e-3, bufs)
+        sbp.accumulate_grads(acc, bufs, first=(k == 0))
+        A = OS.accumulate(A, OS.reduce_peers(H.host_peers(13, 2, k, R, n, 1e-3)))
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_f32(acc), A, f"accumulate R={R} n={n}")
+
+
+def _state(seed, n):
+    th = synth.normal_f32(seed, synth.master_stream(0), n, 0.02)
+    return th, np.zeros(n, np.float32), np.zeros(n, np.float32)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 7, 8, 16])
+@pytest.mark.parametrize("n", SIZES + [BIG])
+@pytest.mark.parametrize("with_acc", [False, True])
+def test_adamw_shard(R, n, with_acc):
+    import torch
+    if n == BIG and R not in (8,):
+        pytest.skip("big size runs at R=8 only")
+    steps = 3
+    th, m, v = _state(14, n)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    pw, dp, g = H.guarded(n, 2)
+    bufs = None
+    acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if with_acc else None
+    scale = sbp.mean_scale(R, 2 if with_acc else 1)
+    want = (th, m, v, None)
+    for t in range(1, steps + 1):
+        acc_h = None
+        if with_acc:  # one earlier microbatch accumulated, the last one fused
+            bufs = H.dev_peers(14, t, 0, R, n, 1e-3, bufs)
+            sbp.accumulate_grads(acc_d, bufs, first=True)
+            acc_h = OS.reduce_peers(H.host_peers(14, t, 0, R, n, 1e-3))
+        bufs = H.dev_peers(14, t, 1, R, n, 1e-3, bufs)
+        sbp.adamw_shard(bufs, acc_d, scale, dth, dm, dv, dp, HP, t)
+        want = OS.shard_step(H.host_peers(14, t, 1, R, n, 1e-3), acc_h, np.float32(scale),
+                             want[0], want[1], want[2], HP, t)
+    torch.cuda.synchronize()
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    worst = H.assert_state_close(got, want, f"adamw R={R} n={n} acc={with_acc}")
+    assert worst == 0, f"expected bit-exact, worst {worst} ulp"
+    assert H.canaries_intact(pw, g)
+
+
+def test_adamw_shard_acc_only():
+    """R = 0: the accumulator carries the whole gradient."""
+    import torch
+    n = 5003
+    th, m, v = _state(15, n)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    dp = H.empty_u16(n)
+    acc = torch.empty(n, dtype=torch.float32, device=H.dev())
+    sbp.accumulate_grads(acc, H.dev_peers(15, 1, 0, 4, n, 1e-3), first=True)
+    sbp.adamw_shard([], acc, 0.25, dth, dm, dv, dp, HP, 1)
+    torch.cuda.synchronize()
+    A = OS.reduce_peers(H.host_peers(15, 1, 0, 4, n, 1e-3))
+    want = OS.shard_step([], A, np.float32(0.25), th, m, v, HP, 1)
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    assert H.assert_state_close(got, want, "acc only") == 0
+
+
+def test_empty_inputs_touch_nothing():
+    import torch
+    whole, out, g = H.guarded(0, 4)
+    p = [H.empty_u16(8)]
+    sbp.reduce_shard([x[:0] for x in p], 1.0, out)
+    st = [torch.zeros(0, dtype=torch.float32, device=H.dev()) for _ in range(3)]
+    sbp.adamw_shard([x[:0] for x in p], None, 1.0, *st, H.empty_u16(0), HP, 1)
+    torch.cuda.synchronize()
+    assert H.canaries_intact(whole, g)
+
+
+def _special_bf16(n, rng):
+    """bf16 patterns with zeros of both signs, subnormals, the largest finite
+    values, infinities and NaNs mixed into ordinary values."""
+    base = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x7F7F,
+                         0xFF7F, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x3F80, 0x3F81, 0x4B80],
+                        dtype=np.uint16)
+    pick = rng.random(n) < 0.3
+    base[pick] = rng.choice(specials, pick.sum())
+    return base
+
+
+def test_special_values():
+    import torch
+    rng = np.random.default_rng(5)
+    n, R = 4099, 3
+    hp = [_special_bf16(n, rng) for _ in range(R)]
+    th = (rng.normal(size=n) * 0.02).astype(np.float32)
+    th[:50] = np.array([0.0, -0.0, 1e-40, -1e-40, 3e38] * 10, dtype=np.float32)
+    m = (rng.normal(size=n) * 1e-3).astype(np.float32)
+    v = np.abs(rng.normal(size=n) * 1e-6).astype(np.float32)
+    v[::7] = 0.0
+    v[1::11] = 1e-42  # subnormal second moment
+    dpe = [H.from_np_u16(x) for x in hp]
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    dp = H.empty_u16(n)
+    out = torch.empty(n, dtype=torch.float32, device=H.dev())
+    sbp.reduce_shard(dpe, 0.5, out)
+    sbp.adamw_shard(dpe, None, 0.5, dth, dm, dv, dp, HP, 7)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        S = OS.normalise(OS.reduce_peers(hp), np.float32(0.5))
+        want = OS.shard_step(hp, None, np.float32(0.5), th, m, v, HP, 7)
+    d = H.ulp_f32(H.to_np_f32(out), S)
+    assert d.max() == 0
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    assert H.assert_state_close(got, want, "special values") == 0
+    # finite results are bit-identical; NaN results agree by class
+    fin = np.isfinite(want[0])
+    H.assert_bits_equal(got[0][fin], want[0][fin], "finite master")
+    H.assert_bits_equal(got[3][fin], want[3][fin], "finite params")
+    assert np.array_equal(np.isnan(got[0]), np.isnan(want[0]))
+    assert np.array_equal(np.isnan(H.to_np_f32(out)), np.isnan(S))
+
+
+# ---- pack --------------------------------------------------------------------
+
+def _pack_case(numels, cap, N, align=8, misalign=False, seed=3):
+    import torch
+    pl = sbp.bucket_plan(numels, cap, N, align)
+    opl = OP.bucket_plan(numels, cap, N, align)
+    grads_h = [synth.normal_bf16(seed, synth.tensor_stream(1, 0, 0, t), n, 1e-2)
+               for t, n in enumerate(numels)]
+    grads_d = []
+    keep = []
+    for gh in grads_h:
+        if misalign and gh.size:
+            base = torch.empty(gh.size + 3, dtype=torch.int16, device=H.dev())
+            view = base[3:]  # 6 bytes past a 16-byte boundary
+            view.copy_(H.from_np_u16(gh))
+            keep.append(base)
+            grads_d.append(view)
+        else:
+            grads_d.append(H.from_np_u16(gh) if gh.size else H.empty_u16(0))
+    return pl, opl, grads_h, grads_d, keep
+
+
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("align", [8, 1])
+def test_pack_ragged(misalign, align):
+    import torch
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
+    pl, opl, gh, gd, keep = _pack_case(numels, 600, 4, align, misalign)
+    whole, flat, g = H.guarded(pl.flat_numel, 2)
+    flat.fill_(0x7777)  # stale contents the pack must overwrite, padding included
+    sbp.pack_grads(pl, gd, flat)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(flat), OS.pack(opl, gh), "pack all")
+    assert H.canaries_intact(whole, g)
+
+
+def test_pack_one_bucket_at_a_time():
+    import torch
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
+    pl, opl, gh, gd, keep = _pack_case(numels, 600, 4)
+    flat = H.empty_u16(pl.flat_numel)
+    flat.fill_(0x7777)
+    want = OS.pack(opl, gh)
+    for b in range(pl.num_buckets):
+        sbp.pack_grads(pl, [gd[t] if t in pl.bucket_tensors(b) else None
+                            for t in range(len(numels))], flat, bucket=b)
+        torch.cuda.synchronize()
+        got = H.to_np_u16(flat)
+        info = pl.bucket(b)
+        end = info["flat_offset"] + info["padded"]
+        H.assert_bits_equal(got[:end], want[:end], f"bucket {b}")
+        assert np.all(got[end:] == 0x7777)  # later buckets untouched
+
+
+def test_pack_big_tensors_many_launches():
+    """More segments than one launch carries, and chunks of multi-MB tensors."""
+    import torch
+    numels = [4096, 3 * 2 ** 20 + 8, 1000] * 40 + [5]
+    pl, opl, gh, gd, keep = _pack_case(numels, 1 << 20, 8)
+    flat = H.empty_u16(pl.flat_numel)
+    sbp.pack_grads(pl, gd, flat)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(flat), OS.pack(opl, gh), "pack big")
