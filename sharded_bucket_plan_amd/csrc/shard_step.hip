@@ -12,14 +12,22 @@
 // Design.  Every kernel here is a single pass over HBM with no reuse, so it
 // is bandwidth-bound (about 0.5 flop per byte against a ridge near 20):
 //   - each lane owns 8 consecutive elements: one 16-byte load per bf16 peer,
-//     two 16-byte loads per fp32 stream, 16-byte stores;
-//   - all loads of a group are issued before any arithmetic, so a lane has
-//     R + 6 (fused) independent 16-byte requests in flight;
+//     two 16-byte loads per fp32 stream, 16-byte stores; all loads of a lane
+//     are issued before any arithmetic;
 //   - R is a template parameter so the peer loop unrolls and the peer
 //     pointers stay in scalar registers (passed by value in the kernel
-//     arguments); no LDS is needed;
-//   - grid-stride over 8-element groups with a grid sized from the CU count;
-//     the n % 8 tail is done element-wise by the first block;
+//     arguments);
+//   - one pass: one 256-lane block per tile of 2048 elements, dispatched in
+//     an XCD-contiguous order (blocks are handed to the 8 XCDs round-robin,
+//     so block b works on tile (b mod 8) * T/8 + b / 8 and each XCD sweeps
+//     its own contiguous eighth of every stream);
+//   - the mix of 11-15 read and write streams runs fastest on MI355X when
+//     each CU keeps about 56 KB of loads in flight; more outstanding
+//     requests congest HBM.  The launch reserves LDS (unused by the kernels)
+//     to hold each CU to the number of blocks that gives that depth for the
+//     kernel's bytes per lane -- a persistent grid measured slower than
+//     letting the dispatcher refill CUs tile by tile;
+//   - the n % 8 tail is done element-wise by the first block;
 //   - binary32 arithmetic with no contraction (also compiled with
 //     -ffp-contract=off): peer sums in ascending order seeded by peer 0,
 //     correctly rounded sqrt and divide, so results match a scalar
@@ -30,14 +38,48 @@
 
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "internal.h"
 
 #pragma clang fp contract(off)
 
+// Build-time tuning knobs (defaults measured best on MI355X): loads in
+// flight per CU that the occupancy cap aims at (KiB; 0 = no cap), the
+// XCD-contiguous tile order, and nontemporal hints on streaming loads/stores.
+#ifndef SBP_INFLIGHT_KB
+#define SBP_INFLIGHT_KB 56
+#endif
+#ifndef SBP_XCD_ORDER
+#define SBP_XCD_ORDER 1
+#endif
+#ifndef SBP_NT_LOAD
+#define SBP_NT_LOAD 0
+#endif
+#ifndef SBP_NT_STORE
+#define SBP_NT_STORE 0
+#endif
+
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kXcds = 8;
+constexpr bool kNtLoad = SBP_NT_LOAD != 0;
+constexpr bool kNtStore = SBP_NT_STORE != 0;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  if constexpr (kNtLoad) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void stg(T* p, T v) {
+  if constexpr (kNtStore) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 struct Peers {
   const uint16_t* p[SBP_MAX_PEERS];
@@ -72,22 +114,31 @@ __device__ __forceinline__ void adamw_one(float g, float& th, float& m, float& v
   v = v1;
 }
 
+// Group (8 elements) handled by this lane, tiles in XCD-contiguous order.
+// A bijection on [0, gridDim.x): the last gridDim.x % 8 tiles keep their place.
+__device__ __forceinline__ int64_t my_group() {
+  unsigned b = blockIdx.x;
+  if (SBP_XCD_ORDER) {
+    const unsigned per = gridDim.x / kXcds;
+    if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+  }
+  return static_cast<int64_t>(b) * kBlock + threadIdx.x;
+}
+
 // Widen peer 0's 8 bf16 values and add peers 1..R-1 in ascending order.
 template <int R>
-__device__ __forceinline__ void peer_sum8(const uint4 (&w)[R], float (&S)[8]) {
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
+__device__ __forceinline__ void peer_sum8(const u32x4 (&w)[R], float (&S)[8]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    S[2 * q] = bf16_lo(w0[q]);
-    S[2 * q + 1] = bf16_hi(w0[q]);
+    S[2 * q] = bf16_lo(w[0][q]);
+    S[2 * q + 1] = bf16_hi(w[0][q]);
   }
 #pragma unroll
   for (int r = 1; r < R; ++r) {
-    const uint32_t* wr = reinterpret_cast<const uint32_t*>(&w[r]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      S[2 * q] = S[2 * q] + bf16_lo(wr[q]);
-      S[2 * q + 1] = S[2 * q + 1] + bf16_hi(wr[q]);
+      S[2 * q] = S[2 * q] + bf16_lo(w[r][q]);
+      S[2 * q + 1] = S[2 * q + 1] + bf16_hi(w[r][q]);
     }
   }
 }
@@ -101,22 +152,25 @@ __device__ __forceinline__ float peer_sum1(const Peers& P, int64_t i) {
 }
 
 __device__ __forceinline__ void load8(const float* p, int64_t gi, float (&x)[8]) {
-  const float4* q = reinterpret_cast<const float4*>(p) + 2 * gi;
-  float4 a = q[0], b = q[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  const f32x4* q = reinterpret_cast<const f32x4*>(p) + 2 * gi;
+  f32x4 a = ldg(q), b = ldg(q + 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
+  }
 }
 
 __device__ __forceinline__ void store8(float* p, int64_t gi, const float (&x)[8]) {
-  float4* q = reinterpret_cast<float4*>(p) + 2 * gi;
-  q[0] = make_float4(x[0], x[1], x[2], x[3]);
-  q[1] = make_float4(x[4], x[5], x[6], x[7]);
+  f32x4* q = reinterpret_cast<f32x4*>(p) + 2 * gi;
+  stg(q, f32x4{x[0], x[1], x[2], x[3]});
+  stg(q + 1, f32x4{x[4], x[5], x[6], x[7]});
 }
 
 template <int R>
-__device__ __forceinline__ void load_peers(const Peers& P, int64_t gi, uint4 (&w)[R]) {
+__device__ __forceinline__ void load_peers(const Peers& P, int64_t gi, u32x4 (&w)[R]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) w[r] = reinterpret_cast<const uint4*>(P.p[r])[gi];
+  for (int r = 0; r < R; ++r) w[r] = ldg(reinterpret_cast<const u32x4*>(P.p[r]) + gi);
 }
 
 // ---- reduce: out = fl(S * scale) ------------------------------------------
@@ -124,10 +178,9 @@ template <int R>
 __global__ void __launch_bounds__(kBlock)
 reduce_kernel(Peers P, float scale, float* __restrict__ out, int64_t n) {
   const int64_t groups = n >> 3;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < groups;
-       gi += stride) {
-    uint4 w[R];
+  const int64_t gi = my_group();
+  if (gi < groups) {
+    u32x4 w[R];
     load_peers<R>(P, gi, w);
     float S[8];
     peer_sum8<R>(w, S);
@@ -146,10 +199,9 @@ template <int R, bool FIRST>
 __global__ void __launch_bounds__(kBlock)
 accumulate_kernel(Peers P, float* __restrict__ acc, int64_t n) {
   const int64_t groups = n >> 3;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < groups;
-       gi += stride) {
-    uint4 w[R];
+  const int64_t gi = my_group();
+  if (gi < groups) {
+    u32x4 w[R];
     load_peers<R>(P, gi, w);
     float A[8];
     if (!FIRST) load8(acc, gi, A);
@@ -179,10 +231,9 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
                    Scalars s) {
   static_assert(R > 0 || ACC, "R == 0 needs the accumulator");
   const int64_t groups = n >> 3;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t gi = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; gi < groups;
-       gi += stride) {
-    uint4 w[R > 0 ? R : 1];
+  const int64_t gi = my_group();
+  if (gi < groups) {
+    u32x4 w[R > 0 ? R : 1];
     if constexpr (R > 0) load_peers<R>(P, gi, w);
     float A[8], th[8], m[8], v[8];
     if (ACC) load8(acc, gi, A);
@@ -209,9 +260,9 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
     store8(master, gi, th);
     store8(mom1, gi, m);
     store8(mom2, gi, v);
-    reinterpret_cast<uint4*>(pout)[gi] =
-        make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                   pb[6] | (pb[7] << 16));
+    stg(reinterpret_cast<u32x4*>(pout) + gi,
+        u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+              pb[6] | (pb[7] << 16)});
   }
   if (blockIdx.x == 0) {
     const int64_t i = (groups << 3) + threadIdx.x;
@@ -235,28 +286,67 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
 
 // ---- launch helpers ---------------------------------------------------------
 
-int cu_count() {
+struct DeviceInfo {
+  int cus = 0;
+  int lds_per_cu = 0;
+};
+
+DeviceInfo device_info() {
   static std::mutex mu;
-  static int cached[64] = {0};
+  static DeviceInfo cached[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceInfo{256, 0};
   std::lock_guard<std::mutex> lock(mu);
-  if (cached[dev] == 0) {
-    int cus = 0;
+  DeviceInfo& d = cached[dev];
+  if (d.cus == 0) {
+    int cus = 0, lds = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        lds < 0)
+      lds = 0;
+    d.cus = cus;
+    d.lds_per_cu = lds;
   }
-  return cached[dev];
+  return d;
 }
 
-// Blocks for a grid-stride pass over `groups` 8-element groups.
-unsigned grid_for(int64_t groups) {
-  const int64_t want = (groups + kBlock - 1) / kBlock;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * 32;
-  int64_t g = want < cap ? want : cap;
-  return static_cast<unsigned>(g < 1 ? 1 : g);
+struct Launch {
+  unsigned grid;
+  unsigned lds;  // dynamic LDS reserved per block to cap blocks per CU
+};
+
+// One block per 2048-element tile; `lane_bytes` = bytes one lane loads.
+Launch launch_for(int64_t n, int lane_bytes) {
+  const int64_t groups = n >> 3;
+  const int64_t tiles = (groups + kBlock - 1) / kBlock;
+  Launch L{static_cast<unsigned>(tiles < 1 ? 1 : tiles), 0};
+  const DeviceInfo d = device_info();
+  if (SBP_INFLIGHT_KB > 0 && d.lds_per_cu > 0) {
+    const int64_t per_block = static_cast<int64_t>(lane_bytes) * kBlock;
+    int64_t blocks_per_cu =
+        (static_cast<int64_t>(SBP_INFLIGHT_KB) * 1024 + per_block / 2) / per_block;
+    if (blocks_per_cu < 1) blocks_per_cu = 1;
+    if (blocks_per_cu < 8)  // beyond that the cap no longer binds
+      // 256 bytes of slack so exactly blocks_per_cu reservations fit a CU
+      L.lds = static_cast<unsigned>(d.lds_per_cu / blocks_per_cu - 256);
+  }
+  return L;
+}
+
+// Large dynamic LDS needs the kernel's limit raised (idempotent, cheap).
+template <typename K>
+sbp_status allow_lds(K kernel, unsigned lds) {
+  if (lds <= 65536) return SBP_OK;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess)
+    return sbp::fail(SBP_EHIP,
+                     std::string("raising the kernel's LDS limit failed: ") + hipGetErrorString(e));
+  return SBP_OK;
 }
 
 sbp_status launched(const char* who) {
@@ -322,6 +412,17 @@ Scalars adamw_scalars(const sbp_adamw_hparams& hp) {
   return s;
 }
 
+// Launches kernel K with the tile grid and occupancy cap for `lane_bytes`.
+template <typename K, typename... Args>
+sbp_status launch(const char* who, K kernel, int64_t n, int lane_bytes, hipStream_t stream,
+                  Args... args) {
+  const Launch L = launch_for(n, lane_bytes);
+  sbp_status st = allow_lds(kernel, L.lds);
+  if (st != SBP_OK) return st;
+  hipLaunchKernelGGL(kernel, dim3(L.grid), dim3(kBlock), L.lds, stream, args...);
+  return launched(who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,14 +430,16 @@ extern "C" {
 sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n, float scale,
                             float* out, hipStream_t stream) {
   const char* who = "sbp_reduce_shard";
-  if (R < 1 || R > SBP_MAX_PEERS) return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: R must be in 1..16");
+  if (R < 1 || R > SBP_MAX_PEERS)
+    return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: R must be in 1..16");
   if (n < 0) return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: n < 0");
   if (n == 0) return sbp::ok();  // nothing is read or written
   Peers P;
   sbp_status st = collect_peers(who, peers, R, P);
   if (st != SBP_OK) return st;
   if (out == nullptr) return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: out is null");
-  if (!sbp::aligned(out, 16)) return sbp::fail(SBP_EALIGN, "sbp_reduce_shard: out not 16-B aligned");
+  if (!sbp::aligned(out, 16))
+    return sbp::fail(SBP_EALIGN, "sbp_reduce_shard: out not 16-B aligned");
   if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_reduce_shard: n too large");
   for (int32_t r = 0; r < R; ++r)
     if (sbp::overlaps(out, 4 * n, peers[r], 2 * n))
@@ -347,9 +450,7 @@ sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n, floa
     if constexpr (RR == 0) {
       return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: R must be >= 1");
     } else {
-      hipLaunchKernelGGL(reduce_kernel<RR>, dim3(grid_for(n >> 3)), dim3(kBlock), 0, stream, P,
-                         scale, out, n);
-      return launched(who);
+      return launch(who, reduce_kernel<RR>, n, 16 * RR, stream, P, scale, out, n);
     }
   });
 }
@@ -376,14 +477,10 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers, int32_t R,
     constexpr int RR = decltype(rc)::value;
     if constexpr (RR == 0) {
       return sbp::fail(SBP_EINVAL, "sbp_accumulate_grads: R must be >= 1");
+    } else if (first) {
+      return launch(who, accumulate_kernel<RR, true>, n, 16 * RR, stream, P, acc, n);
     } else {
-      if (first)
-        hipLaunchKernelGGL((accumulate_kernel<RR, true>), dim3(grid_for(n >> 3)), dim3(kBlock), 0,
-                           stream, P, acc, n);
-      else
-        hipLaunchKernelGGL((accumulate_kernel<RR, false>), dim3(grid_for(n >> 3)), dim3(kBlock),
-                           0, stream, P, acc, n);
-      return launched(who);
+      return launch(who, accumulate_kernel<RR, false>, n, 16 * RR + 32, stream, P, acc, n);
     }
   });
 }
@@ -426,22 +523,20 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc
         return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: buffers overlap");
   const Scalars s = adamw_scalars(*hp);
   uint16_t* pout = static_cast<uint16_t*>(param_out);
+  const int lane_bytes = 16 * R + 96 + (acc ? 32 : 0);
   (void)hipGetLastError();
-  const unsigned grid = grid_for(n >> 3);
   return dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
     if constexpr (RR == 0) {
-      hipLaunchKernelGGL((fused_adamw_kernel<0, true>), dim3(grid), dim3(kBlock), 0, stream, P,
-                         acc, scale, master, m, v, pout, n, s);
+      return launch(who, fused_adamw_kernel<0, true>, n, lane_bytes, stream, P, acc, scale,
+                    master, m, v, pout, n, s);
+    } else if (acc) {
+      return launch(who, fused_adamw_kernel<RR, true>, n, lane_bytes, stream, P, acc, scale,
+                    master, m, v, pout, n, s);
     } else {
-      if (acc)
-        hipLaunchKernelGGL((fused_adamw_kernel<RR, true>), dim3(grid), dim3(kBlock), 0, stream,
-                           P, acc, scale, master, m, v, pout, n, s);
-      else
-        hipLaunchKernelGGL((fused_adamw_kernel<RR, false>), dim3(grid), dim3(kBlock), 0, stream,
-                           P, acc, scale, master, m, v, pout, n, s);
+      return launch(who, fused_adamw_kernel<RR, false>, n, lane_bytes, stream, P, acc, scale,
+                    master, m, v, pout, n, s);
     }
-    return launched(who);
   });
 }
 
