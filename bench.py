@@ -37,7 +37,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("params updated/sec and HBM GB/s (% of 8 TB/s roofline), fused shard step")
 PEAK_GBS = 8000.0  # MI355X HBM3E
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_adamw_llama3_8b_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_adamw_llama3_8b_pmc.md")
+COPY_BYTES = 1 << 32  # the calibration copy moves 4 GiB in and 4 GiB out
+CALIBRATION_CALLS = 4  # --calibrate-copy: one warm-up copy + 3 timed ones
 KERNEL_SRC = os.path.join(ROOT, "sharded_bucket_plan_amd", "csrc", "shard_step.hip")
 
 
@@ -50,7 +52,8 @@ def kernel_source_hash():
     with open(KERNEL_SRC, "rb") as f:
         h.update(f.read())
     from sharded_bucket_plan_amd.build import FLAGS
-    h.update(" ".join(FLAGS).encode())
+    # the flags minus absolute paths (the tree lives elsewhere on other machines)
+    h.update(" ".join(f for f in FLAGS if not os.path.isabs(f)).encode())
     return h.hexdigest()
 
 
@@ -124,23 +127,42 @@ class Workload:
             return self.sbp.tokens_scale([self.synth.tokens(self.seed, t, r) for r in range(w.R)])
         return self.sbp.mean_scale(w.R, w.K)
 
+    def parts(self):
+        """Kernel groups of one step with their algorithmic bytes."""
+        w, n = self.w, self.n
+        out = []
+        if w.pack:
+            out.append(("pack_kernel", 4 * sum(w.numels) + 2 * (self.plan.flat_numel - sum(w.numels))))
+        if self.acc:
+            out.append(("accumulate_kernel", (2 * w.R + 4) * n + (2 * w.R + 8) * n * (w.K - 2)))
+        out.append(("fused_adamw_kernel", self.bytes_fused))
+        return out
+
     def step(self, t, ev=None):
-        """One whole per-step path; ev = (start, end) events around the fused launch."""
+        """One whole per-step path; ev = {part: (start, end)} events around each
+        kernel group (on the stream the kernels are launched on)."""
         s = self.sets[self.i]
         self.i = (self.i + 1) % self.nsets
         sbp, w = self.sbp, self.w
+
+        def mark(part, k):
+            if ev:
+                ev[part][k].record()
+
         if w.pack:
+            mark("pack_kernel", 0)
             sbp.pack_grads(self.plan, s["grads"], s["flat0"])
+            mark("pack_kernel", 1)
         if self.acc:
+            mark("accumulate_kernel", 0)
             for k in range(w.K - 1):
                 sbp.accumulate_grads(s["acc"], s["mb"][k], first=(k == 0))
+            mark("accumulate_kernel", 1)
         scale = self.scale(t)
-        if ev:
-            ev[0].record()
+        mark("fused_adamw_kernel", 0)
         sbp.adamw_shard(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"], s["p"],
                         self.hp, t)
-        if ev:
-            ev[1].record()
+        mark("fused_adamw_kernel", 1)
 
     def config(self):
         w = self.w
@@ -151,19 +173,130 @@ class Workload:
                 "fused_bytes_per_elem": fused_bytes_per_elem(w.R, self.acc)}
 
 
+def _summary_fields(path):
+    """`key: value` lines of a profile summary."""
+    out = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(("#", "|", " ")):
+                k, v = ln.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
 def traffic_from_profile(nbytes_per_launch):
     """HBM bytes per fused launch from the committed counter summary, if it was
     taken on the current kernel source and the same workload size."""
     try:
-        with open(PMC_SUMMARY) as f:
-            d = json.load(f)
-    except (OSError, ValueError):
+        d = _summary_fields(PMC_SUMMARY)
+    except OSError:
         return None
     if d.get("source_sha256") != kernel_source_hash():
         return None
-    if d.get("algorithmic_bytes_per_launch") != nbytes_per_launch:
+    if d.get("algorithmic_bytes_per_launch") != str(nbytes_per_launch):
         return None
-    return d.get("traffic_bytes_per_launch")
+    try:
+        return int(d["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_ceiling_gbs(reps=5):
+    """A plain streaming copy of 4 GiB on this GPU (bytes read + written / time).
+
+    An elementwise kernel (dst = -src) rather than copy_(), which torch hands
+    to the runtime's memcpy; it is the only dispatch here, so the same call
+    under rocprofv3 --pmc calibrates the byte counters."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, value) of every dispatch in rocprofv3 counter CSVs under d."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, command):
+    """Write the committed HBM-traffic summary of the fused kernel from four
+    rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, on the benchmark and on
+    the 4 GiB calibration copy).  Counter values are KiB per dispatch."""
+    import statistics
+
+    def per(rows, key):
+        v = [x for k, x in rows if key in k]
+        if not v:
+            raise SystemExit(f"no dispatch of {key} in the counter files")
+        return statistics.median(v), len(v)
+
+    f_k, nf = per(_pmc_rows(fetch_dir, "FETCH_SIZE"), "fused_adamw_kernel")
+    w_k, nw = per(_pmc_rows(write_dir, "WRITE_SIZE"), "fused_adamw_kernel")
+    # calibration: --calibrate-copy makes CALIBRATION_CALLS copies that each read
+    # and write COPY_BYTES (torch may split one copy into several dispatches, so
+    # counters are summed over all of them)
+    cf = sum(x for _, x in _pmc_rows(copy_fetch_dir, "FETCH_SIZE"))
+    cw = sum(x for _, x in _pmc_rows(copy_write_dir, "WRITE_SIZE"))
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no calibration dispatches in the counter files")
+    known = CALIBRATION_CALLS * COPY_BYTES
+    f_scale = known / (cf * 1024)
+    w_scale = known / (cw * 1024)
+    fetch_b = f_k * 1024 * f_scale
+    write_b = w_k * 1024 * w_scale
+    import synth
+    import sharded_bucket_plan_amd as sbp
+    w = synth.WORKLOADS["llama3_8b"]
+    n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+    alg = fused_bytes_per_elem(w.R, False) * n
+    alg_read = (2 * w.R + 12) * n
+    alg_write = 14 * n
+    lines = [
+        "# fused_adamw_kernel, llama3_8b shard (n = %d, R = %d): HBM traffic" % (n, w.R),
+        "",
+        "Commands (rocprofv3, one counter per run):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| FETCH_SIZE per fused dispatch (KiB, median of {nf}) | {f_k:.0f} |",
+        f"| WRITE_SIZE per fused dispatch (KiB, median of {nw}) | {w_k:.0f} |",
+        f"| calibration: {CALIBRATION_CALLS} copies of {COPY_BYTES} B each way; summed FETCH_SIZE / WRITE_SIZE (KiB) | {cf:.0f} / {cw:.0f} |",
+        f"| scale factors (known bytes / counted bytes) fetch, write | {f_scale:.4f}, {w_scale:.4f} |",
+        f"| fused reads: counted x scale / algorithmic | {fetch_b:.4g} / {alg_read} = {fetch_b / alg_read:.4f} |",
+        f"| fused writes: counted x scale / algorithmic | {write_b:.4g} / {alg_write} = {write_b / alg_write:.4f} |",
+        "",
+        f"source_sha256: {kernel_source_hash()}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
+    ]
+    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
+    with open(PMC_SUMMARY, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(workload_name, seed, target_s):
@@ -209,7 +342,17 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the 4 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "CMD"),
+                    help="write the HBM-traffic summary from rocprofv3 counter runs")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -223,6 +366,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
+                          "bytes_each_way": COPY_BYTES, "calls": CALIBRATION_CALLS}))
+        return
     log(f"bench: workload {args.workload}, allocating and generating inputs on cuda:0")
     W = Workload(args.workload, seed)
     log(f"bench: n={W.n} R={W.w.R} sets={W.nsets}; warmup {args.warmup}")
@@ -231,8 +378,9 @@ def main():
         t += 1
         W.step(t)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    parts = W.parts()
+    evs = [{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for p, _ in parts} for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -244,14 +392,29 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kernels = {}
+    for p, nbytes in parts:
+        ms = [e[p][0].elapsed_time(e[p][1]) for e in evs]
+        avg = sum(ms) / len(ms)
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        kernels[p] = {"ms_avg": avg, "ms_min": min(ms), "algorithmic_bytes": nbytes,
+                      "gbs": gbs, "frac": gbs / PEAK_GBS}
+    kern_ms = [e["fused_adamw_kernel"][0].elapsed_time(e["fused_adamw_kernel"][1]) for e in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
     achieved = W.bytes_fused / (kern_avg * 1e-3) / 1e9
     value = W.n / (ms_per_step * 1e-3)
+    config = W.config()
+    bytes_fused = W.bytes_fused
     log(f"bench: {ms_per_step:.4f} ms/step, fused kernel {kern_avg:.4f} ms avg "
         f"(min {min(kern_ms):.4f}), {achieved:.1f} GB/s algorithmic")
 
-    traffic = traffic_from_profile(W.bytes_fused)
+    traffic = traffic_from_profile(bytes_fused)
+    copy_gbs = None
+    if not args.no_copy_ceiling:
+        del W
+        torch.cuda.empty_cache()
+        copy_gbs = copy_ceiling_gbs()
+        log(f"bench: 4 GiB device copy on this GPU: {copy_gbs:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: CPU baseline (~{args.cpu_seconds:.0f} s of oracle work)")
@@ -270,12 +433,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": W.config(),
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBS, "traffic": traffic,
                      "kernel": "fused_adamw_kernel", "kernel_ms_avg": kern_avg,
-                     "algorithmic_bytes_per_launch": W.bytes_fused},
+                     "algorithmic_bytes_per_launch": bytes_fused,
+                     "copy_gbs_this_gpu": copy_gbs,
+                     "frac_of_copy": (achieved / copy_gbs) if copy_gbs else None},
         "cpu_baseline": cpu,
+        "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
 
