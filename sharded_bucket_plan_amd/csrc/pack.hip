@@ -6,17 +6,18 @@
 // is: a persistent, caller-owned buffer written in place).
 //
 // Design (CDNA4).  A bucket mixes 4096-element norm vectors with matrices
-// of half a billion elements, so work is cut into equal chunks of 8192
-// elements (16 KB), not per tensor:
+// of half a billion elements, so work is cut into equal chunks of
+// 2048 * kRounds elements, not per tensor:
 //   - the host lists the bucket(s) as segments -- a tensor copy, or a run of
 //     zero padding -- each with the index of its first chunk; up to
 //     kMaxSegs segments travel by value in the kernel arguments (no device
 //     allocation, nothing to upload), longer lists take several launches;
-//   - a block grid-strides over chunks and finds its segment by binary
-//     search over the chunk starts (uniform per block, so it runs on scalar
-//     loads of the kernel arguments);
-//   - a chunk is 4 rounds of 256 lanes x 16 bytes: fully coalesced 16-byte
-//     loads and stores when the source is 16-byte aligned and the
+//   - one pass: one block per chunk, in XCD-contiguous order (as the
+//     streaming kernels), and it finds its segment by binary search over
+//     the chunk starts (uniform per block, so it runs on scalar loads of the
+//     kernel arguments);
+//   - a chunk is kRounds rounds of 256 lanes x 16 bytes: fully coalesced
+//     16-byte loads and stores when the source is 16-byte aligned and the
 //     destination offset a multiple of 8 elements; otherwise element-wise.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,8 +29,13 @@
 
 namespace {
 
+#ifndef SBP_PACK_ROUNDS
+#define SBP_PACK_ROUNDS 1
+#endif
+
 constexpr int kBlock = 256;
-constexpr int kRounds = 4;
+constexpr int kRounds = SBP_PACK_ROUNDS;
+constexpr int kXcds = 8;
 constexpr int64_t kChunk = static_cast<int64_t>(kBlock) * 8 * kRounds;  // elements
 constexpr int kMaxSegs = 96;
 
@@ -56,7 +62,12 @@ __device__ __forceinline__ int find_seg(const SegList& L, int64_t c) {
 }
 
 __global__ void __launch_bounds__(kBlock) pack_kernel(SegList L, uint16_t* __restrict__ flat) {
-  for (int64_t c = blockIdx.x; c < L.chunks; c += gridDim.x) {
+  // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
+  unsigned b = blockIdx.x;
+  const unsigned per = gridDim.x / kXcds;
+  if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+  {
+    const int64_t c = b;
     const Seg sg = L.seg[find_seg(L, c)];
     const int64_t start = (c - sg.first_chunk) * kChunk;
     const int64_t rem = sg.len - start;
@@ -80,15 +91,6 @@ __global__ void __launch_bounds__(kBlock) pack_kernel(SegList L, uint16_t* __res
       for (int64_t j = threadIdx.x; j < cnt; j += kBlock) d[j] = s ? s[j] : 0;
     }
   }
-}
-
-int cu_count_pack() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 256;
-  return cus;
 }
 
 }  // namespace
@@ -135,7 +137,6 @@ extern "C" sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
   }
 
   (void)hipGetLastError();
-  const int64_t grid_cap = static_cast<int64_t>(cu_count_pack()) * 16;
   for (size_t i = 0; i < segs.size(); i += kMaxSegs) {
     SegList L;
     L.count = 0;
@@ -146,9 +147,10 @@ extern "C" sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
       L.chunks += (s.len + kChunk - 1) / kChunk;
       L.seg[L.count++] = s;
     }
-    const int64_t g = L.chunks < grid_cap ? L.chunks : grid_cap;
-    hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream, L,
-                       static_cast<uint16_t*>(flat));
+    if (L.chunks > 0x7FFFFFFF)
+      return sbp::fail(SBP_ERANGE, "sbp_pack_grads: too many chunks for one launch");
+    hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(L.chunks)), dim3(kBlock), 0, stream,
+                       L, static_cast<uint16_t*>(flat));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
       return sbp::fail(SBP_EHIP, std::string("sbp_pack_grads: launch failed: ") +
