@@ -18,7 +18,8 @@ Modules:
   plan   bucket plan: per-tensor offsets in flat buckets, padding, per-rank
          chunks, shard map, model-state byte accounting
   step   pack / chunk / gather, ascending-rank reduce, accumulate, normalise,
-         AdamW, bf16 cast, and the whole shard step composed from them
+         AdamW, bf16 cast, the whole shard step composed from them, and
+         global gradient-norm clipping (squared norm, coefficient, scale)
 
 Every function is pinned by tests/test_oracle_*.py against closed forms,
 invariants, special cases, library routines or brute force; none is

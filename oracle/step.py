@@ -211,6 +211,34 @@ def adamw(theta, m, v, g, sc):
     return theta1, m1, v1
 
 
+# ---- global gradient-norm clipping -------------------------------------------------
+
+CLIP_EPS = 1e-6  # added to the norm before dividing (the common convention)
+
+
+def grad_sq_norm(G, scale):
+    """Sum over this rank's shard of g*g, g = fl(G*scale), in float64.
+
+    "Parallelisms", section ZeRO-2: global gradient-norm clipping needs the
+    norm over all gradient shards before any weight is updated, and only an
+    all-reduce of local squared norms.  Each square of a binary32 value is
+    exact in float64; math.fsum gives the correctly rounded float64 sum.
+    """
+    g = normalise(G, scale).astype(np.float64)
+    return math.fsum((g * g).tolist())
+
+
+def clip_coef(total_sq, max_norm):
+    """min(1, max_norm / (||g|| + eps)), in float64; ||g|| = sqrt(total of the
+    ranks' squared norms)."""
+    return min(1.0, float(max_norm) / (math.sqrt(total_sq) + CLIP_EPS))
+
+
+def clipped_scale(scale, coef):
+    """The clip coefficient folded into the normalisation: fl32(scale * coef)."""
+    return F32(float(F32(scale)) * coef)
+
+
 # ---- the whole shard step ----------------------------------------------------------
 
 def shard_step(peers, acc, scale, theta, m, v, hp, t):

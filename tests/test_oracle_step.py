@@ -8,6 +8,7 @@ shard updates equals the unsharded update), and library routines (torch's
 bf16 conversion, torch.optim.AdamW).
 """
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -461,3 +462,65 @@ def test_shard_step_composition_and_bf16_emit():
     # emitted bf16 differs from the master by at most half a bf16 ulp
     back = S.bf16_to_f32(p).astype(np.float64)
     assert np.all(np.abs(back - th) <= ulp32(th) * 2 ** 15 * 1.0000001 + 1e-45)
+
+
+# ---- global gradient-norm clipping ----------------------------------------------
+
+def test_grad_sq_norm_exact_and_sharded():
+    """The squared norm is the correctly rounded float64 sum of exact squares;
+    summing the shards' squared norms (the all-reduce the page asks for)
+    gives the unsharded norm."""
+    numels, pl = _ragged_plan(N=4)
+    R = 3
+    flats = [S.pack(pl, [synth.normal_bf16(6, synth.tensor_stream(1, 0, r, t), n, 1e-2)
+                         for t, n in enumerate(numels)]) for r in range(R)]
+    scale = S.mean_scale(R)
+    G_full = S.reduce_peers(flats)
+    full = S.grad_sq_norm(G_full, scale)
+    g = S.normalise(G_full, scale)
+    exact = sum(Fraction(float(x)) ** 2 for x in g)
+    assert full == float(exact)  # fsum rounds the exact sum once
+    parts = [S.grad_sq_norm(S.reduce_peers([S.chunk(pl, f, s) for f in flats]), scale)
+             for s in range(pl.world_n)]
+    assert abs(sum(parts) - full) <= 4 * 2.0 ** -53 * full
+    # padding contributes nothing; zero gradient has zero norm
+    assert S.grad_sq_norm(np.zeros(10, np.float32), scale) == 0.0
+
+
+def test_clip_coefficient_and_clipped_norm():
+    n = 4096
+    G = S.reduce_peers([synth.normal_bf16(8, synth.peer_stream(1, 0, r), n, 1e-1)
+                        for r in range(2)])
+    scale = S.mean_scale(2)
+    sq = S.grad_sq_norm(G, scale)
+    norm = math.sqrt(sq)
+    assert S.clip_coef(sq, 10 * norm) == 1.0  # below the threshold: untouched
+    assert S.clipped_scale(scale, 1.0) == scale
+    max_norm = norm / 4
+    c = S.clip_coef(sq, max_norm)
+    assert abs(c - max_norm / norm) <= 1e-6 / norm * c + 1e-15
+    cs = S.clipped_scale(scale, c)
+    clipped = math.sqrt(S.grad_sq_norm(G, cs))
+    assert abs(clipped / max_norm - 1) < 1e-6  # the clipped gradient has the target norm
+
+
+def test_clip_matches_torch_clip_grad_norm():
+    """torch.nn.utils.clip_grad_norm_ (fp32 norm, same coefficient rule)."""
+    n = 1 << 14
+    G = S.reduce_peers([synth.normal_bf16(9, synth.peer_stream(1, 0, r), n, 1e-1)
+                        for r in range(4)])
+    scale = S.mean_scale(4)
+    g = S.normalise(G, scale)
+    for max_norm in (0.05, 0.5, 50.0):
+        p = torch.nn.Parameter(torch.zeros(n))
+        p.grad = torch.from_numpy(g.copy())
+        total = torch.nn.utils.clip_grad_norm_([p], max_norm)
+        sq = S.grad_sq_norm(G, scale)
+        assert abs(float(total) - math.sqrt(sq)) <= 1e-6 * math.sqrt(sq)
+        ref = p.grad.numpy().astype(np.float64)
+        ours = S.normalise(G, S.clipped_scale(scale, S.clip_coef(sq, max_norm)))
+        # torch's norm is an fp32 reduction (about 1e-6 relative), ours exact
+        assert np.all(np.abs(ours - ref) <= 2e-6 * np.abs(ref) + 1e-30)
+        if max_norm == 50.0:  # no clipping: identical to the unclipped gradient
+            assert np.array_equal(ours, g)
+
