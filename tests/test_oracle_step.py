@@ -502,6 +502,8 @@ def test_clip_coefficient_and_clipped_norm():
     cs = S.clipped_scale(scale, c)
     clipped = math.sqrt(S.grad_sq_norm(G, cs))
     assert abs(clipped / max_norm - 1) < 1e-6  # the clipped gradient has the target norm
+    assert math.isnan(S.clip_coef(float("nan"), 1.0))  # NaN propagates
+    assert S.clip_coef(float("inf"), 1.0) == 0.0
 
 
 def test_clip_matches_torch_clip_grad_norm():
