@@ -64,7 +64,7 @@ def fused_bytes_per_elem(R, acc):
 class Workload:
     """Device buffers and the per-step launches of one workload."""
 
-    def __init__(self, name, seed):
+    def __init__(self, name, seed, clip=None):
         import torch
         import sharded_bucket_plan_amd as sbp
         import synth
@@ -79,7 +79,10 @@ class Workload:
         self.plan = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
         self.n = self.plan.shard_numel
         self.acc = w.K > 1
-        self.bytes_fused = fused_bytes_per_elem(w.R, self.acc) * self.n
+        self.clip = clip
+        # with clipping the update reads G (fp32) written by the norm pass
+        self.bytes_fused = (fused_bytes_per_elem(0, True) if clip else
+                            fused_bytes_per_elem(w.R, self.acc)) * self.n
         mall = 256 << 20
         set_bytes = self.bytes_fused
         self.nsets = 1 if set_bytes >= 4 * mall else max(2, -(-4 * mall // set_bytes))
@@ -119,6 +122,11 @@ class Workload:
             s["peers"] = s["mb"][-1]
         if self.acc:
             s["acc"] = self._f32(n)
+        if self.clip:
+            s["gsum"] = self._f32(n)
+            s["ws"] = self.torch.empty(self.sbp.grad_sq_norm_workspace(n),
+                                       dtype=self.torch.float64, device=self.dev)
+            s["sq"] = self.torch.empty(1, dtype=self.torch.float64, device=self.dev)
         return s
 
     def scale(self, t):
@@ -135,6 +143,8 @@ class Workload:
             out.append(("pack_kernel", 4 * sum(w.numels) + 2 * (self.plan.flat_numel - sum(w.numels))))
         if self.acc:
             out.append(("accumulate_kernel", (2 * w.R + 4) * n + (2 * w.R + 8) * n * (w.K - 2)))
+        if self.clip:
+            out.append(("sq_norm_kernel", (2 * w.R + (4 if self.acc else 0) + 4) * n))
         out.append(("fused_adamw_kernel", self.bytes_fused))
         return out
 
@@ -159,6 +169,17 @@ class Workload:
                 sbp.accumulate_grads(s["acc"], s["mb"][k], first=(k == 0))
             mark("accumulate_kernel", 1)
         scale = self.scale(t)
+        if self.clip:
+            # this rank's squared norm; with more ranks its all-reduce goes here
+            mark("sq_norm_kernel", 0)
+            sbp.grad_sq_norm(s["peers"], s.get("acc"), scale, self.n, g_sum_out=s["gsum"],
+                             workspace=s["ws"], sq_out=s["sq"])
+            mark("sq_norm_kernel", 1)
+            scale, _ = sbp.clip_scale(s["sq"].item(), self.clip, scale)
+            mark("fused_adamw_kernel", 0)
+            sbp.adamw_shard([], s["gsum"], scale, s["master"], s["m"], s["v"], s["p"], self.hp, t)
+            mark("fused_adamw_kernel", 1)
+            return
         mark("fused_adamw_kernel", 0)
         sbp.adamw_shard(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"], s["p"],
                         self.hp, t)
@@ -170,7 +191,8 @@ class Workload:
                 "N": w.world_n, "K": w.K, "norm": w.norm,
                 "bucket_cap_MiB": w.bucket_cap_bytes >> 20, "buckets": self.plan.num_buckets,
                 "pack": w.pack, "rotating_buffer_sets": self.nsets,
-                "fused_bytes_per_elem": fused_bytes_per_elem(w.R, self.acc)}
+                "clip_max_norm": self.clip,
+                "fused_bytes_per_elem": self.bytes_fused // self.n}
 
 
 def _summary_fields(path):
@@ -341,6 +363,8 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--clip", type=float, default=None, metavar="MAX_NORM",
+                    help="add global gradient-norm clipping to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -371,7 +395,7 @@ def main():
                           "bytes_each_way": COPY_BYTES, "calls": CALIBRATION_CALLS}))
         return
     log(f"bench: workload {args.workload}, allocating and generating inputs on cuda:0")
-    W = Workload(args.workload, seed)
+    W = Workload(args.workload, seed, args.clip)
     log(f"bench: n={W.n} R={W.w.R} sets={W.nsets}; warmup {args.warmup}")
     t = 0
     for _ in range(args.warmup):

@@ -254,6 +254,42 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R,
                            float* m, float* v, void* param_out, int64_t n,
                            const sbp_adamw_hparams* hp, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Global gradient-norm clipping ("Parallelisms", ZeRO-2: clipping needs the
+ * norm over all gradient shards before any weight is updated, and only an
+ * all-reduce of the ranks' local squared norms).
+ *
+ * sbp_grad_sq_norm: this rank's squared norm of the normalised gradient,
+ *   sum_i (double) g_i^2 with g_i = fl(G_i * scale), G as in sbp_adamw_shard
+ *   (G = acc + S, S, or acc when R == 0), accumulated in float64 (each square
+ *   is exact) in a fixed order: one partial per 2048-element tile in
+ *   `workspace`, then those partials in index order into *sq_out (device).
+ *   Results are deterministic run to run.  If g_sum_out is given, G (fp32,
+ *   unscaled) is also written there, so the update can follow as
+ *   sbp_adamw_shard(R = 0, acc = g_sum_out, scale = clipped scale) without
+ *   reading the peers again.
+ *   peers, R, acc, scale, n   as in sbp_adamw_shard (R may be 0 with acc)
+ *   g_sum_out                 device fp32[n], 16-B aligned, or null
+ *   workspace                 device double[workspace_len], 8-B aligned,
+ *                             workspace_len >= sbp_grad_sq_norm_workspace(n)
+ *   sq_out                    device double, 8-B aligned (n == 0 writes 0)
+ *   Outputs must not overlap any other buffer.
+ *   Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE, SBP_EHIP.
+ *
+ * sbp_clip_scale (host): with total_sq the sum of all ranks' squared norms,
+ *   coef = min(1, max_norm / (sqrt(total_sq) + 1e-6)) in float64 (a NaN norm
+ *   gives a NaN coefficient), *clipped_scale = fl32(scale * coef), and
+ *   *coef (optional) receives coef.  Errors: SBP_EINVAL (null output).
+ * ---------------------------------------------------------------------- */
+int64_t sbp_grad_sq_norm_workspace(int64_t n);
+sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R,
+                            const float* acc, float scale, int64_t n,
+                            float* g_sum_out, double* workspace,
+                            int64_t workspace_len, double* sq_out,
+                            hipStream_t stream);
+sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale,
+                          float* clipped_scale, double* coef);
+
 #ifdef __cplusplus
 }
 #endif

@@ -230,9 +230,9 @@ def grad_sq_norm(G, scale):
 
 def clip_coef(total_sq, max_norm):
     """min(1, max_norm / (||g|| + eps)), in float64; ||g|| = sqrt(total of the
-    ranks' squared norms).  A NaN norm gives a NaN coefficient (no skip
-    policy: NaN propagates)."""
-    q = float(max_norm) / (math.sqrt(total_sq) + CLIP_EPS)
+    ranks' squared norms).  max_norm is a binary32 hyperparameter, like lr.
+    A NaN norm gives a NaN coefficient (no skip policy: NaN propagates)."""
+    q = float(F32(max_norm)) / (math.sqrt(total_sq) + CLIP_EPS)
     return q if (q < 1.0 or math.isnan(q)) else 1.0
 
 

@@ -8,7 +8,7 @@ call fails, an error is raised.
 
 Functions (same names as the C calls without the "sbp_" prefix):
   bucket_plan, pack_grads, reduce_shard, accumulate_grads, adamw_shard,
-  mean_scale, tokens_scale.
+  mean_scale, tokens_scale, grad_sq_norm, clip_scale.
 """
 
 import ctypes
@@ -29,6 +29,7 @@ EXPORTS = (
     "sbp_plan_shard_numel", "sbp_plan_flat_numel", "sbp_plan_tensor", "sbp_plan_bucket",
     "sbp_plan_bucket_tensors", "sbp_plan_state_bytes", "sbp_mean_scale", "sbp_tokens_scale",
     "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
+    "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
 )
 
 
@@ -87,6 +88,12 @@ def lib():
         "sbp_adamw_shard": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_int64, ctypes.POINTER(AdamWHParams), ctypes.c_void_p], st),
+        "sbp_grad_sq_norm_workspace": ([ctypes.c_int64], ctypes.c_int64),
+        "sbp_grad_sq_norm": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                              ctypes.c_void_p, ctypes.c_void_p], st),
+        "sbp_clip_scale": ([ctypes.c_double, ctypes.c_float, ctypes.c_float,
+                            ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -289,3 +296,46 @@ def adamw_shard(peers, acc, scale, master, m, v, param_out, hp, step, stream=Non
         _f32(master, "adamw_shard master"), _f32(m, "adamw_shard m"), _f32(v, "adamw_shard v"),
         _dev(param_out, 2, "adamw_shard param_out"), n, ctypes.byref(h),
         _stream(stream, master)))
+
+
+def grad_sq_norm_workspace(n):
+    """Doubles of workspace sbp_grad_sq_norm needs for n elements."""
+    return int(lib().sbp_grad_sq_norm_workspace(int(n)))
+
+
+def grad_sq_norm(peers, acc, scale, n, g_sum_out=None, workspace=None, sq_out=None,
+                 stream=None):
+    """sbp_grad_sq_norm: this rank's squared norm of g = fl(G*scale) (float64).
+
+    Returns the device tensor holding it (float64[1]); workspace and sq_out are
+    allocated with torch when not given.  With g_sum_out, G is written too.
+    """
+    import torch
+    ref = peers[0] if peers else acc
+    dev = ref.device
+    if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
+        raise ValueError("grad_sq_norm: peers/acc differ in size")
+    if g_sum_out is not None and g_sum_out.numel() != n:
+        raise ValueError("grad_sq_norm: g_sum_out has the wrong size")
+    if workspace is None:
+        workspace = torch.empty(grad_sq_norm_workspace(n), dtype=torch.float64, device=dev)
+    if sq_out is None:
+        sq_out = torch.empty(1, dtype=torch.float64, device=dev)
+    for t, what in ((workspace, "workspace"), (sq_out, "sq_out")):
+        if t.dtype != torch.float64 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"grad_sq_norm: {what} must be a contiguous float64 device tensor")
+    _check(lib().sbp_grad_sq_norm(
+        _ptrs(peers, "grad_sq_norm peers"), len(peers),
+        None if acc is None else _f32(acc, "grad_sq_norm acc"), float(scale), int(n),
+        None if g_sum_out is None else _f32(g_sum_out, "grad_sq_norm g_sum_out"),
+        workspace.data_ptr(), workspace.numel(), sq_out.data_ptr(), _stream(stream, ref)))
+    return sq_out
+
+
+def clip_scale(total_sq, max_norm, scale):
+    """sbp_clip_scale: (fl32(scale * coef), coef), coef = min(1, max/(||g||+1e-6))."""
+    out = ctypes.c_float()
+    coef = ctypes.c_double()
+    _check(lib().sbp_clip_scale(float(total_sq), float(max_norm), float(scale),
+                                ctypes.byref(out), ctypes.byref(coef)))
+    return out.value, coef.value

@@ -284,6 +284,94 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
   }
 }
 
+// ---- squared norm of g = fl(G*scale) in fp64 (for global-norm clipping) -----
+// Deterministic: a fixed order within a lane, a fixed shuffle tree within a
+// wave, waves in order within a block, one partial per tile, and the tile
+// partials summed in a fixed order by sq_finalize_kernel.
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = x + __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Sum of x over the block, in a fixed order; valid in thread 0.
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double per_wave[kBlock / 64];
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) per_wave[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) t = t + per_wave[w];
+  }
+  return t;
+}
+
+template <int R, bool ACC, bool WRITE>
+__global__ void __launch_bounds__(kBlock)
+sq_norm_kernel(Peers P, const float* __restrict__ acc, float scale, float* __restrict__ gsum,
+               int64_t n, double* __restrict__ partial) {
+  static_assert(R > 0 || ACC, "R == 0 needs the accumulator");
+  const int64_t groups = n >> 3;
+  const int64_t gi = my_group();
+  double local = 0.0;
+  if (gi < groups) {
+    u32x4 w[R > 0 ? R : 1];
+    if constexpr (R > 0) load_peers<R>(P, gi, w);
+    float A[8];
+    if (ACC) load8(acc, gi, A);
+    float G[8];
+    if constexpr (R > 0) {
+      peer_sum8<R>(w, G);
+      if (ACC) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) G[j] = A[j] + G[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) G[j] = A[j];
+    }
+    if (WRITE) store8(gsum, gi, G);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double g = static_cast<double>(G[j] * scale);
+      local = local + g * g;
+    }
+  }
+  if (blockIdx.x == 0) {
+    const int64_t i = (groups << 3) + threadIdx.x;
+    if (i < n) {
+      float G;
+      if constexpr (R > 0) {
+        G = peer_sum1<R>(P, i);
+        if (ACC) G = acc[i] + G;
+      } else {
+        G = acc[i];
+      }
+      if (WRITE) gsum[i] = G;
+      const double g = static_cast<double>(G * scale);
+      local = local + g * g;
+    }
+  }
+  const double t = block_sum(local);
+  if (threadIdx.x == 0) {
+    unsigned b = blockIdx.x;  // this block's tile, the index of its partial
+    const unsigned per = gridDim.x / kXcds;
+    if (SBP_XCD_ORDER && b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+    partial[b] = t;
+  }
+}
+
+__global__ void __launch_bounds__(kBlock)
+sq_finalize_kernel(const double* __restrict__ partial, int64_t count, double* __restrict__ out) {
+  double t = 0.0;
+  for (int64_t i = threadIdx.x; i < count; i += kBlock) t = t + partial[i];
+  t = block_sum(t);
+  if (threadIdx.x == 0) out[0] = t;
+}
+
 // ---- launch helpers ---------------------------------------------------------
 
 struct DeviceInfo {
@@ -318,11 +406,15 @@ struct Launch {
   unsigned lds;  // dynamic LDS reserved per block to cap blocks per CU
 };
 
+// Tiles (one 256-lane block each) covering n elements; at least one.
+int64_t tiles_for(int64_t n) {
+  const int64_t tiles = ((n >> 3) + kBlock - 1) / kBlock;
+  return tiles < 1 ? 1 : tiles;
+}
+
 // One block per 2048-element tile; `lane_bytes` = bytes one lane loads.
 Launch launch_for(int64_t n, int lane_bytes) {
-  const int64_t groups = n >> 3;
-  const int64_t tiles = (groups + kBlock - 1) / kBlock;
-  Launch L{static_cast<unsigned>(tiles < 1 ? 1 : tiles), 0};
+  Launch L{static_cast<unsigned>(tiles_for(n)), 0};
   const DeviceInfo d = device_info();
   if (SBP_INFLIGHT_KB > 0 && d.lds_per_cu > 0) {
     const int64_t per_block = static_cast<int64_t>(lane_bytes) * kBlock;
@@ -330,8 +422,9 @@ Launch launch_for(int64_t n, int lane_bytes) {
         (static_cast<int64_t>(SBP_INFLIGHT_KB) * 1024 + per_block / 2) / per_block;
     if (blocks_per_cu < 1) blocks_per_cu = 1;
     if (blocks_per_cu < 8)  // beyond that the cap no longer binds
-      // 256 bytes of slack so exactly blocks_per_cu reservations fit a CU
-      L.lds = static_cast<unsigned>(d.lds_per_cu / blocks_per_cu - 256);
+      // 512 bytes of slack so exactly blocks_per_cu reservations fit a CU,
+      // together with the few bytes of static LDS the norm kernels use
+      L.lds = static_cast<unsigned>(d.lds_per_cu / blocks_per_cu - 512);
   }
   return L;
 }
@@ -538,6 +631,92 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc
                     master, m, v, pout, n, s);
     }
   });
+}
+
+int64_t sbp_grad_sq_norm_workspace(int64_t n) { return n < 0 ? -1 : tiles_for(n); }
+
+sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* acc, float scale,
+                            int64_t n, float* g_sum_out, double* workspace,
+                            int64_t workspace_len, double* sq_out, hipStream_t stream) {
+  const char* who = "sbp_grad_sq_norm";
+  if (R < 0 || R > SBP_MAX_PEERS)
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: R must be in 0..16");
+  if (n < 0) return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: n < 0");
+  if (sq_out == nullptr || workspace == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: null workspace or result pointer");
+  if (!sbp::aligned(sq_out, 8) || !sbp::aligned(workspace, 8))
+    return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: workspace and result must be 8-byte aligned");
+  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm: n too large");
+  const int64_t need = tiles_for(n);
+  if (workspace_len < need)
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: workspace too small (see "
+                                 "sbp_grad_sq_norm_workspace)");
+  if (sbp::overlaps(sq_out, 8, workspace, 8 * need))
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: result overlaps the workspace");
+  (void)hipGetLastError();
+  if (n == 0) {  // the squared norm of nothing is 0
+    hipLaunchKernelGGL(sq_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, workspace,
+                       int64_t{0}, sq_out);
+    return launched(who);
+  }
+  Peers P;
+  sbp_status st = collect_peers(who, peers, R, P);
+  if (st != SBP_OK) return st;
+  if (R == 0 && acc == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: R == 0 needs an accumulator");
+  if ((acc && !sbp::aligned(acc, 16)) || (g_sum_out && !sbp::aligned(g_sum_out, 16)))
+    return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: device arrays must be 16-byte aligned");
+  // outputs (g_sum_out, workspace, sq_out) must not overlap any other buffer
+  const void* ptr[4 + SBP_MAX_PEERS];
+  int64_t len[4 + SBP_MAX_PEERS];
+  int k = 0;
+  ptr[k] = g_sum_out; len[k++] = g_sum_out ? 4 * n : 0;
+  ptr[k] = workspace; len[k++] = 8 * need;
+  ptr[k] = sq_out; len[k++] = 8;
+  ptr[k] = acc; len[k++] = acc ? 4 * n : 0;
+  for (int32_t r = 0; r < R; ++r) { ptr[k] = peers[r]; len[k++] = 2 * n; }
+  for (int a = 0; a < 3; ++a)
+    for (int b = a + 1; b < k; ++b)
+      if (sbp::overlaps(ptr[a], len[a], ptr[b], len[b]))
+        return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: buffers overlap");
+  const int lane_bytes = 16 * R + (acc ? 32 : 0);
+  st = dispatch_r(R, [&](auto rc) -> sbp_status {
+    constexpr int RR = decltype(rc)::value;
+    const bool wr = g_sum_out != nullptr;
+    if constexpr (RR == 0) {
+      if (wr)
+        return launch(who, sq_norm_kernel<0, true, true>, n, lane_bytes, stream, P, acc, scale,
+                      g_sum_out, n, workspace);
+      return launch(who, sq_norm_kernel<0, true, false>, n, lane_bytes, stream, P, acc, scale,
+                    g_sum_out, n, workspace);
+    } else if (acc) {
+      if (wr)
+        return launch(who, sq_norm_kernel<RR, true, true>, n, lane_bytes, stream, P, acc, scale,
+                      g_sum_out, n, workspace);
+      return launch(who, sq_norm_kernel<RR, true, false>, n, lane_bytes, stream, P, acc, scale,
+                    g_sum_out, n, workspace);
+    } else {
+      if (wr)
+        return launch(who, sq_norm_kernel<RR, false, true>, n, lane_bytes, stream, P, acc,
+                      scale, g_sum_out, n, workspace);
+      return launch(who, sq_norm_kernel<RR, false, false>, n, lane_bytes, stream, P, acc, scale,
+                    g_sum_out, n, workspace);
+    }
+  });
+  if (st != SBP_OK) return st;
+  hipLaunchKernelGGL(sq_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, workspace, need,
+                     sq_out);
+  return launched(who);
+}
+
+sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale, float* clipped_scale,
+                          double* coef) {
+  if (clipped_scale == nullptr) return sbp::fail(SBP_EINVAL, "sbp_clip_scale: null output");
+  const double q = static_cast<double>(max_norm) / (sqrt(total_sq) + 1e-6);
+  const double c = (q < 1.0 || q != q) ? q : 1.0;  // NaN propagates
+  *clipped_scale = static_cast<float>(static_cast<double>(scale) * c);
+  if (coef) *coef = c;
+  return sbp::ok();
 }
 
 }  // extern "C"

@@ -164,3 +164,41 @@ def test_device_calls_validate_before_launch():
     assert pack(plan.handle, -1, (V * 2)(0x100001, 0x200000), V(0x300000), None) == sbp.SBP_EALIGN
     assert pack(plan.handle, -1, (V * 2)(None, 0x200000), V(0x300000), None) == sbp.SBP_EINVAL
     assert pack(plan.handle, -1, grads, V(0x100000 + 16), None) == sbp.SBP_EINVAL  # overlap
+
+
+def test_clip_scale_matches_oracle():
+    import math
+    from oracle import step as OS
+    import numpy as np
+    rng = np.random.default_rng(4)
+    for _ in range(2000):
+        sq = float(rng.choice([0.0, 1e-30, 1e-6, 1.0, 123.4, 1e12])) * float(rng.random())
+        mx = float(np.float32(rng.choice([1e-3, 0.5, 1.0, 5.0])))
+        sc = float(OS.mean_scale(int(rng.integers(1, 9))))
+        got, coef = sbp.clip_scale(sq, mx, sc)
+        want_coef = OS.clip_coef(sq, mx)
+        assert coef == want_coef
+        assert got == float(OS.clipped_scale(sc, want_coef))
+    got, coef = sbp.clip_scale(float("nan"), 1.0, 0.5)
+    assert math.isnan(coef) and math.isnan(got)
+    assert sbp.clip_scale(float("inf"), 1.0, 0.5) == (0.0, 0.0)
+
+
+def test_grad_sq_norm_validates_before_launch():
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    peers = (V * 2)(0x100000, 0x200000)
+    n = 10000
+    need = sbp.grad_sq_norm_workspace(n)
+    assert need == (n // 8 + 255) // 256 and sbp.grad_sq_norm_workspace(0) == 1
+    f = L.sbp_grad_sq_norm
+    ws, sq = V(0x800000), V(0x900000)
+    assert f(peers, 2, None, 1.0, n, None, None, need, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, None, ws, need - 1, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, None, ws, need, V(0x900004), None) == sbp.SBP_EALIGN
+    assert f(peers, 0, None, 1.0, n, None, ws, need, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 17, None, 1.0, n, None, ws, need, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, V(0x300008), ws, need, sq, None) == sbp.SBP_EALIGN
+    assert f(peers, 2, None, 1.0, n, V(0x100000), ws, need, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, None, ws, need, V(0x800000), None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, -1, None, ws, need, sq, None) == sbp.SBP_EINVAL

@@ -256,3 +256,79 @@ def test_pack_big_tensors_many_launches():
     sbp.pack_grads(pl, gd, flat)
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_u16(flat), OS.pack(opl, gh), "pack big")
+
+
+# ---- global gradient-norm clipping ---------------------------------------------
+
+@pytest.mark.parametrize("R", [0, 1, 3, 8])
+@pytest.mark.parametrize("n", [1, 9, 2047, 256 * 8 * 3 + 5, BIG])
+@pytest.mark.parametrize("write", [False, True])
+def test_grad_sq_norm(R, n, write):
+    import torch
+    if n == BIG and R not in (8,):
+        pytest.skip("big size runs at R=8 only")
+    bufs = H.dev_peers(21, 1, 0, R, n, 1e-3) if R else []
+    acc_d = None
+    acc_h = None
+    if R == 0 or R == 3:  # with an accumulator of an earlier microbatch
+        acc_d = torch.empty(n, dtype=torch.float32, device=H.dev())
+        sbp.accumulate_grads(acc_d, H.dev_peers(21, 1, 1, 2, n, 1e-3), first=True)
+        acc_h = OS.reduce_peers(H.host_peers(21, 1, 1, 2, n, 1e-3))
+    scale = sbp.mean_scale(max(R, 1), 2)
+    whole, gsum, g = H.guarded(n, 4)
+    sq = sbp.grad_sq_norm(bufs, acc_d, scale, n, g_sum_out=gsum if write else None)
+    sq2 = sbp.grad_sq_norm(bufs, acc_d, scale, n)
+    torch.cuda.synchronize()
+    if R:
+        S = OS.reduce_peers(H.host_peers(21, 1, 0, R, n, 1e-3))
+        G = S if acc_h is None else acc_h + S
+    else:
+        G = acc_h
+    want = OS.grad_sq_norm(G, np.float32(scale))
+    got = float(sq.item())
+    assert abs(got - want) <= 1e-13 * want, (got, want)
+    assert got == float(sq2.item())  # deterministic run to run
+    if write:
+        H.assert_bits_equal(H.to_np_f32(gsum), G, "g_sum_out")
+        assert H.canaries_intact(whole, g)
+
+
+def test_grad_sq_norm_empty():
+    import torch
+    sq = torch.full((1,), 7.0, dtype=torch.float64, device=H.dev())
+    sbp.grad_sq_norm([H.empty_u16(0)], None, 1.0, 0, sq_out=sq)
+    torch.cuda.synchronize()
+    assert sq.item() == 0.0
+
+
+@pytest.mark.parametrize("max_norm", [1e-3, 1e3])
+def test_clipped_step_two_shards(max_norm):
+    """Two ranks' shards: local squared norms (the all-reduce is their sum), a
+    clip scale from the total, then the update from the stored G with R = 0.
+    Compared with the oracle's clipping of the same gradients."""
+    import torch
+    R, n, hp = 4, 40000 + 3, HP
+    scale = sbp.mean_scale(R)
+    shards = []
+    total = 0.0
+    for s in range(2):
+        peers = H.dev_peers(22 + s, 1, 0, R, n, 1e-2)
+        G = torch.empty(n, dtype=torch.float32, device=H.dev())
+        total += sbp.grad_sq_norm(peers, None, scale, n, g_sum_out=G).item()
+        shards.append(G)
+    cs, coef = sbp.clip_scale(total, max_norm, scale)
+    Gh = [OS.reduce_peers(H.host_peers(22 + s, 1, 0, R, n, 1e-2)) for s in range(2)]
+    want_total = sum(OS.grad_sq_norm(x, np.float32(scale)) for x in Gh)
+    assert abs(total - want_total) <= 1e-13 * want_total
+    want_cs = OS.clipped_scale(scale, OS.clip_coef(want_total, max_norm))
+    assert cs == float(want_cs)
+    assert (coef < 1.0) == (max_norm < 1.0)
+    for s in range(2):
+        th, m, v = _state(30 + s, n)
+        dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+        dp = H.empty_u16(n)
+        sbp.adamw_shard([], shards[s], cs, dth, dm, dv, dp, hp, 1)
+        torch.cuda.synchronize()
+        want = OS.shard_step([], Gh[s], want_cs, th, m, v, hp, 1)
+        got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+        assert H.assert_state_close(got, want, f"clipped shard {s}") == 0
