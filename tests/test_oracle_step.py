@@ -496,9 +496,9 @@ def test_clip_coefficient_and_clipped_norm():
     norm = math.sqrt(sq)
     assert S.clip_coef(sq, 10 * norm) == 1.0  # below the threshold: untouched
     assert S.clipped_scale(scale, 1.0) == scale
-    max_norm = norm / 4
+    max_norm = float(np.float32(norm / 4))  # a binary32 hyperparameter
     c = S.clip_coef(sq, max_norm)
-    assert abs(c - max_norm / norm) <= 1e-6 / norm * c + 1e-15
+    assert c == max_norm / (norm + 1e-6)
     cs = S.clipped_scale(scale, c)
     clipped = math.sqrt(S.grad_sq_norm(G, cs))
     assert abs(clipped / max_norm - 1) < 1e-6  # the clipped gradient has the target norm
