@@ -263,7 +263,9 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R,
  *   sum_i (double) g_i^2 with g_i = fl(G_i * scale), G as in sbp_adamw_shard
  *   (G = acc + S, S, or acc when R == 0), accumulated in float64 (each square
  *   is exact) in a fixed order: one partial per 2048-element tile in
- *   `workspace`, then those partials in index order into *sq_out (device).
+ *   `workspace`, then a tree of fixed shape over those partials (groups of
+ *   2048 consecutive partials, level by level, the levels also kept in
+ *   `workspace`) into *sq_out (device).
  *   Results are deterministic run to run.  If g_sum_out is given, G (fp32,
  *   unscaled) is also written there, so the update can follow as
  *   sbp_adamw_shard(R = 0, acc = g_sum_out, scale = clipped scale) without

@@ -287,7 +287,7 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
 // ---- squared norm of g = fl(G*scale) in fp64 (for global-norm clipping) -----
 // Deterministic: a fixed order within a lane, a fixed shuffle tree within a
 // wave, waves in order within a block, one partial per tile, and the tile
-// partials summed in a fixed order by sq_finalize_kernel.
+// partials summed by a tree of fixed shape (partials_sum_kernel levels).
 
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
@@ -364,12 +364,20 @@ sq_norm_kernel(Peers P, const float* __restrict__ acc, float scale, float* __res
   }
 }
 
+// One level of the fixed-shape tree over the partials: block b sums
+// in[b*kFanIn, (b+1)*kFanIn) -- 8 consecutive values per lane in order, then
+// the block sum -- into out[b].
+constexpr int kFanIn = kBlock * 8;
+
 __global__ void __launch_bounds__(kBlock)
-sq_finalize_kernel(const double* __restrict__ partial, int64_t count, double* __restrict__ out) {
+partials_sum_kernel(const double* __restrict__ in, int64_t count, double* __restrict__ out) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kFanIn + threadIdx.x * 8;
   double t = 0.0;
-  for (int64_t i = threadIdx.x; i < count; i += kBlock) t = t + partial[i];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (base + j < count) t = t + in[base + j];
   t = block_sum(t);
-  if (threadIdx.x == 0) out[0] = t;
+  if (threadIdx.x == 0) out[blockIdx.x] = t;
 }
 
 // ---- launch helpers ---------------------------------------------------------
@@ -633,7 +641,37 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc
   });
 }
 
-int64_t sbp_grad_sq_norm_workspace(int64_t n) { return n < 0 ? -1 : tiles_for(n); }
+// Workspace of the squared norm: the tile partials, then each tree level.
+static int64_t sq_norm_workspace(int64_t n) {
+  int64_t count = tiles_for(n), total = count;
+  while (count > kFanIn) {
+    count = (count + kFanIn - 1) / kFanIn;
+    total += count;
+  }
+  return total;
+}
+
+// Sums `count` partials at `ws` into *out with the fixed-shape tree; the
+// levels' outputs go to the workspace right after the partials.
+static sbp_status sum_partials(const char* who, double* ws, int64_t count, double* out,
+                               hipStream_t stream) {
+  double* in = ws;
+  double* next = ws + count;
+  while (count > kFanIn) {
+    const int64_t blocks = (count + kFanIn - 1) / kFanIn;
+    hipLaunchKernelGGL(partials_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       stream, in, count, next);
+    sbp_status st = launched(who);
+    if (st != SBP_OK) return st;
+    in = next;
+    next += blocks;
+    count = blocks;
+  }
+  hipLaunchKernelGGL(partials_sum_kernel, dim3(1), dim3(kBlock), 0, stream, in, count, out);
+  return launched(who);
+}
+
+int64_t sbp_grad_sq_norm_workspace(int64_t n) { return n < 0 ? -1 : sq_norm_workspace(n); }
 
 sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* acc, float scale,
                             int64_t n, float* g_sum_out, double* workspace,
@@ -647,18 +685,15 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
   if (!sbp::aligned(sq_out, 8) || !sbp::aligned(workspace, 8))
     return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: workspace and result must be 8-byte aligned");
   if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm: n too large");
-  const int64_t need = tiles_for(n);
+  const int64_t need = sq_norm_workspace(n);
   if (workspace_len < need)
     return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: workspace too small (see "
                                  "sbp_grad_sq_norm_workspace)");
   if (sbp::overlaps(sq_out, 8, workspace, 8 * need))
     return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: result overlaps the workspace");
   (void)hipGetLastError();
-  if (n == 0) {  // the squared norm of nothing is 0
-    hipLaunchKernelGGL(sq_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, workspace,
-                       int64_t{0}, sq_out);
-    return launched(who);
-  }
+  if (n == 0)  // the squared norm of nothing is 0
+    return sum_partials(who, workspace, 0, sq_out, stream);
   Peers P;
   sbp_status st = collect_peers(who, peers, R, P);
   if (st != SBP_OK) return st;
@@ -704,9 +739,7 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
     }
   });
   if (st != SBP_OK) return st;
-  hipLaunchKernelGGL(sq_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, workspace, need,
-                     sq_out);
-  return launched(who);
+  return sum_partials(who, workspace, tiles_for(n), sq_out, stream);
 }
 
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale, float* clipped_scale,

@@ -191,6 +191,8 @@ def test_grad_sq_norm_validates_before_launch():
     n = 10000
     need = sbp.grad_sq_norm_workspace(n)
     assert need == (n // 8 + 255) // 256 and sbp.grad_sq_norm_workspace(0) == 1
+    tiles = (10 ** 10 // 8 + 255) // 256  # 4882813 tile partials, then 2385, then 2
+    assert sbp.grad_sq_norm_workspace(10 ** 10) == tiles + 2385 + 2
     f = L.sbp_grad_sq_norm
     ws, sq = V(0x800000), V(0x900000)
     assert f(peers, 2, None, 1.0, n, None, None, need, sq, None) == sbp.SBP_EINVAL
