@@ -58,14 +58,25 @@ class Plan:
         return self.buckets[self.tensor_bucket[t]].flat_offset + self.tensor_offset[t]
 
 
-def bucket_plan(numels, cap_bytes, world_n, align=8, order="reverse"):
-    """Assign tensors to flat bf16 buckets and split each bucket into N chunks."""
+def bucket_plan(numels, cap_bytes, world_n, align=8, order="reverse", split=False):
+    """Assign tensors to flat bf16 buckets and split each bucket into N chunks.
+
+    split=False: whole tensors per bucket (the closing rule above).
+    split=True: the tensors are concatenated (each at the first multiple of
+    `align` after the previous one, in visit order) and the result is cut
+    into fixed-size buckets of cap_bytes / 2 elements rounded down to a
+    multiple of align * N (at least align * N); a tensor may then straddle
+    buckets, as when a flat parameter is cut into equal communication
+    pieces.  Only the last bucket can be shorter; it is padded as before.
+    """
     if cap_bytes <= 0 or world_n <= 0 or align <= 0 or (align & (align - 1)):
         raise ValueError("cap_bytes, world_n > 0 and align a power of two required")
     if any(int(x) < 0 for x in numels):
         raise ValueError("negative numel")
     T = len(numels)
     visit = list(range(T - 1, -1, -1)) if order == "reverse" else list(range(T))
+    if split:
+        return _split_plan(numels, cap_bytes, world_n, align, order, visit)
 
     groups = []  # (tensor ids, offsets, used)
     cur, offs, used = [], [], 0
@@ -95,6 +106,37 @@ def bucket_plan(numels, cap_bytes, world_n, align=8, order="reverse"):
         flat_off += padded
     return Plan([int(x) for x in numels], cap_bytes, world_n, align, order,
                 tensor_bucket, tensor_offset, buckets, shard_off, flat_off)
+
+
+def _split_plan(numels, cap_bytes, world_n, align, order, visit):
+    T = len(numels)
+    unit = align * world_n
+    size = max(unit, (cap_bytes // 2) // unit * unit)  # elements per bucket
+    # concatenate in visit order, each tensor at the first aligned slot
+    flat_pos = [None] * T
+    end = 0
+    for t in visit:
+        flat_pos[t] = 0 if end == 0 else _round_up(end, align)
+        end = flat_pos[t] + int(numels[t])
+    nb = -(-end // size) if end > 0 else (1 if T else 0)
+    # a tensor's bucket is the one its first element falls in (the last one
+    # for an empty tensor at the very end)
+    tensor_bucket = [min(flat_pos[t] // size, nb - 1) for t in range(T)]
+    tensor_offset = [flat_pos[t] - tensor_bucket[t] * size for t in range(T)]
+    buckets = []
+    shard_off = 0
+    for b in range(nb):
+        lo, hi = b * size, (b + 1) * size
+        used = max(0, min(hi, end) - lo)
+        padded = _round_up(used, unit)
+        members = [t for t in visit
+                   if (int(numels[t]) > 0 and flat_pos[t] < hi and flat_pos[t] + int(numels[t]) > lo)
+                   or (int(numels[t]) == 0 and tensor_bucket[t] == b)]
+        buckets.append(Bucket(members, used, padded, padded // world_n, shard_off, lo))
+        shard_off += padded // world_n
+    flat = sum(b.padded for b in buckets)
+    return Plan([int(x) for x in numels], cap_bytes, world_n, align, order, tensor_bucket,
+                tensor_offset, buckets, shard_off, flat)
 
 
 # Bytes per parameter of the model state with bf16 params and grads, an fp32

@@ -203,3 +203,65 @@ def test_state_bytes_workload_plans():
     pl = P.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     assert P.state_bytes(pl.flat_numel, pl.shard_numel, 0) == 16 * 8030261248
     assert P.state_bytes(pl.flat_numel, pl.shard_numel, 3) == 16 * 1003782656
+
+
+# ---- fixed-size buckets with tensors split across them ----------------------------
+
+def _check_split_plan(numels, cap, N, align, order):
+    pl = P.bucket_plan(numels, cap, N, align, order, split=True)
+    T = len(numels)
+    unit = align * N
+    size = max(unit, (cap // 2) // unit * unit)
+    visit = list(range(T - 1, -1, -1)) if order == "reverse" else list(range(T))
+    pos = {t: pl.tensor_flat_offset(t) for t in range(T)}
+    # concatenation in visit order at the first aligned slot
+    end = 0
+    for t in visit:
+        want = 0 if end == 0 else -(-end // align) * align
+        assert pos[t] == want
+        end = want + numels[t]
+    total = end
+    # equal buckets of `size` elements, only the last one short (and padded)
+    nb = len(pl.buckets)
+    assert nb == (-(-total // size) if total else (1 if T else 0))
+    for b, bk in enumerate(pl.buckets):
+        assert bk.flat_offset == b * size
+        if b < nb - 1:
+            assert bk.used == bk.padded == size
+        assert bk.padded % unit == 0 and bk.used <= bk.padded < bk.used + unit or bk.used == 0
+        assert bk.chunk * N == bk.padded
+    # every element of a tensor lies in exactly one bucket listing the tensor
+    for t in range(T):
+        for e in range(pos[t], pos[t] + numels[t]):
+            b = e // size
+            assert t in pl.buckets[b].tensors
+        if numels[t]:
+            assert pl.tensor_bucket[t] == pos[t] // size
+    so = 0
+    for bk in pl.buckets:
+        assert bk.shard_offset == so
+        so += bk.chunk
+    assert pl.shard_numel == so and pl.flat_numel == N * so == sum(b.padded for b in pl.buckets)
+    return pl
+
+
+def test_split_plan_properties_brute_force():
+    rng = random.Random(77)
+    for _ in range(1500):
+        T = rng.randint(0, 8)
+        numels = [rng.choice([0, 1, 3, 8, 9, 31, 64, 100]) for _ in range(T)]
+        _check_split_plan(numels, rng.randint(1, 300), rng.choice([1, 2, 3, 4]),
+                          rng.choice([1, 2, 4, 8]), rng.choice(["reverse", "forward"]))
+
+
+def test_split_plan_gpt_7b5_cap_sweep():
+    # every numel of this model is a multiple of 8, so the flat buffer is the plain
+    # concatenation of 6,648,963,072 elements; a c MiB cap gives buckets of
+    # c * 2^19 elements (a multiple of 8 * 64): ceil(6648963072 / (c * 2^19)).
+    w = synth.WORKLOADS["gpt_7b5"]
+    got = {c: len(P.bucket_plan(w.numels, c << 20, 64, split=True).buckets)
+           for c in (1, 2, 4, 8, 16, 32, 64, 128, 256)}
+    assert got == {1: 12682, 2: 6341, 4: 3171, 8: 1586, 16: 793, 32: 397, 64: 199, 128: 100,
+                   256: 50}
+    pl = P.bucket_plan(w.numels, 25 << 20, 64, split=True)
+    assert pl.shard_numel == 103890048  # same shard size as whole-tensor buckets (no padding)
