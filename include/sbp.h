@@ -91,11 +91,19 @@ const char* sbp_version(void);
  *     elements and split into world_n equal chunks; rank s owns chunk s of
  *     every bucket, and its shard is those chunks in bucket order.
  *
+ * With SBP_SPLIT_TENSORS the buckets are instead fixed-size pieces of the
+ * flat buffer: tensors are concatenated (each at the first multiple of
+ * align_elems after the previous one, in visit order) and cut into buckets
+ * of bucket_cap_bytes/2 elements rounded down to a multiple of
+ * align_elems * world_n (at least that); a tensor may straddle buckets, and
+ * only the last bucket can be short (then padded as above).
+ *
  * numel[n_tensors]   element counts in registration order (>= 0 each)
  * bucket_cap_bytes   > 0
  * world_n            shard divisor N, > 0
  * align_elems        power of two, 1..4096 (8 keeps every chunk 16-B aligned)
- * flags              SBP_ORDER_REVERSE (0) or SBP_ORDER_FORWARD
+ * flags              SBP_ORDER_REVERSE (0) or SBP_ORDER_FORWARD, optionally
+ *                    | SBP_SPLIT_TENSORS
  * out                receives an immutable plan; free with sbp_plan_free.
  *                    A plan is read-only after creation and may be shared
  *                    between threads.
@@ -106,6 +114,7 @@ typedef struct sbp_plan sbp_plan;
 
 #define SBP_ORDER_REVERSE 0u
 #define SBP_ORDER_FORWARD 1u
+#define SBP_SPLIT_TENSORS 2u
 
 sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
                            int64_t bucket_cap_bytes, int32_t world_n,
@@ -121,7 +130,8 @@ int32_t sbp_plan_world_n(const sbp_plan* plan);
 int64_t sbp_plan_shard_numel(const sbp_plan* plan);
 /* Elements of the flat buffer holding all buckets (= N * shard numel). */
 int64_t sbp_plan_flat_numel(const sbp_plan* plan);
-/* Tensor t's bucket and its offset inside the bucket. */
+/* Tensor t's bucket and its offset inside the bucket (for a split plan: the
+ * bucket holding its first element). */
 sbp_status sbp_plan_tensor(const sbp_plan* plan, int32_t t, int32_t* bucket,
                            int64_t* offset);
 /* Bucket b: used length, padded length, chunk (= padded / N), start of its
@@ -130,8 +140,9 @@ sbp_status sbp_plan_tensor(const sbp_plan* plan, int32_t t, int32_t* bucket,
 sbp_status sbp_plan_bucket(const sbp_plan* plan, int32_t b, int64_t* used,
                            int64_t* padded, int64_t* chunk,
                            int64_t* shard_offset, int64_t* flat_offset);
-/* Tensor ids of bucket b in the order they were placed; writes up to `cap`
- * ids and returns the bucket's tensor count in *count. */
+/* Tensor ids of bucket b in the order they were placed (for a split plan:
+ * every tensor with an element in the bucket); writes up to `cap` ids and
+ * returns the bucket's tensor count in *count. */
 sbp_status sbp_plan_bucket_tensors(const sbp_plan* plan, int32_t b,
                                    int32_t* ids, int32_t cap, int32_t* count);
 /* Persistent model-state bytes per rank: bf16 params (2) + bf16 grads (2) +
@@ -162,7 +173,9 @@ sbp_status sbp_tokens_scale(const int64_t* counts, int32_t R, float* scale);
  *
  * Copies every tensor of bucket `bucket` (or of all buckets if bucket == -1)
  * bit for bit from tensor_grads[t] to flat[flat_offset_b + offset_t ...],
- * and writes +0 (0x0000) into every other element of those buckets.
+ * and writes +0 (0x0000) into every other element of those buckets.  With a
+ * split plan only the part of a straddling tensor inside the selected
+ * bucket(s) is copied.
  *
  * tensor_grads  host array of plan->n_tensors device pointers to bf16
  *               gradients (2-byte aligned); entries of tensors outside the
@@ -177,6 +190,40 @@ sbp_status sbp_tokens_scale(const int64_t* counts, int32_t R, float* scale);
 sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
                           const void* const* tensor_grads, void* flat,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The all-gather side and the local halves of the collectives
+ * ("Parallelisms", ZeRO-1: reduce-scatter gives each worker the reduced
+ * shard it owns, and an all-gather of the updated shards restores the
+ * complete model; FSDP / Flat parameter: the original parameters are views
+ * into the flat buffer).  Same copy engine and conventions as pack (16-byte
+ * vector path when both sides are 16-B aligned, element-wise otherwise; no
+ * device allocation; bucket = -1 for all buckets).
+ *
+ * sbp_unpack_params: flat bf16 buckets -> per-tensor bf16 parameters: every
+ *   tensor element inside the selected bucket(s) is copied to
+ *   tensor_params[t]; padding is not read.  tensor_params is a host array of
+ *   plan->n_tensors device pointers (2-B aligned; entries of tensors outside
+ *   the selection are not read); they must not overlap each other or flat.
+ * sbp_shard_of: chunk `rank` of every selected bucket of a flat buffer ->
+ *   shard[shard_offset_b ...] (what rank `rank` owns; each rank's flat
+ *   gradient buckets reduce into these shards).  flat: flat_numel elements,
+ *   shard: shard_numel elements, both 16-B aligned, disjoint.
+ * sbp_gather_shards: the N ranks' shards -> flat[flat_offset_b + s*chunk_b
+ *   ...] for every selected bucket: the layout an all-gather of the bf16
+ *   parameter shards produces.  shards: host array of N device pointers
+ *   (16-B aligned, shard_numel elements each), disjoint from flat.
+ * Errors: SBP_EINVAL (null, rank or bucket out of range, overlap),
+ * SBP_EALIGN, SBP_ERANGE, SBP_EHIP.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_unpack_params(const sbp_plan* plan, int32_t bucket,
+                             const void* flat, void* const* tensor_params,
+                             hipStream_t stream);
+sbp_status sbp_shard_of(const sbp_plan* plan, int32_t bucket, int32_t rank,
+                        const void* flat, void* shard, hipStream_t stream);
+sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket,
+                             const void* const* shards, void* flat,
+                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Reduce ("Parallelisms", ZeRO-1: reduce-scatter leaves each worker the

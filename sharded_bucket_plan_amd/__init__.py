@@ -7,8 +7,9 @@ the current HIP stream.  There is no fallback: if libsbp.so is missing, or a
 call fails, an error is raised.
 
 Functions (same names as the C calls without the "sbp_" prefix):
-  bucket_plan, pack_grads, reduce_shard, accumulate_grads, adamw_shard,
-  mean_scale, tokens_scale, grad_sq_norm, clip_scale.
+  bucket_plan, pack_grads, unpack_params, shard_of, gather_shards,
+  reduce_shard, accumulate_grads, adamw_shard, mean_scale, tokens_scale,
+  grad_sq_norm, clip_scale.
 """
 
 import ctypes
@@ -20,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsbp.so")
 
 SBP_OK, SBP_EINVAL, SBP_EALIGN, SBP_ERANGE, SBP_EHIP, SBP_ENOMEM = 0, -1, -2, -3, -4, -5
 SBP_MAX_PEERS = 16
-ORDER_REVERSE, ORDER_FORWARD = 0, 1
+ORDER_REVERSE, ORDER_FORWARD, SPLIT_TENSORS = 0, 1, 2
 
 # every function include/sbp.h declares
 EXPORTS = (
@@ -30,6 +31,7 @@ EXPORTS = (
     "sbp_plan_bucket_tensors", "sbp_plan_state_bytes", "sbp_mean_scale", "sbp_tokens_scale",
     "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
+    "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards",
 )
 
 
@@ -94,6 +96,12 @@ def lib():
                               ctypes.c_void_p, ctypes.c_void_p], st),
         "sbp_clip_scale": ([ctypes.c_double, ctypes.c_float, ctypes.c_float,
                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)], st),
+        "sbp_unpack_params": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, _vpp,
+                               ctypes.c_void_p], st),
+        "sbp_shard_of": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_void_p], st),
+        "sbp_gather_shards": ([ctypes.c_void_p, ctypes.c_int32, _vpp, ctypes.c_void_p,
+                               ctypes.c_void_p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -174,13 +182,17 @@ class Plan:
         return out.value
 
 
-def bucket_plan(numels, bucket_cap_bytes, world_n, align=8, order="reverse"):
-    """sbp_bucket_plan: flat-bucket layout of a parameter list (host only)."""
+def bucket_plan(numels, bucket_cap_bytes, world_n, align=8, order="reverse", split=False):
+    """sbp_bucket_plan: flat-bucket layout of a parameter list (host only).
+
+    split=True: fixed-size buckets with tensors split across them."""
     arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
     h = ctypes.c_void_p()
     flags = ORDER_REVERSE if order == "reverse" else ORDER_FORWARD
     if order not in ("reverse", "forward"):
         flags = 0xFF  # rejected by the library
+    if split:
+        flags |= SPLIT_TENSORS
     _check(lib().sbp_bucket_plan(arr, len(numels), int(bucket_cap_bytes), int(world_n),
                                  int(align), flags, ctypes.byref(h)))
     return Plan(h.value, numels)
@@ -339,3 +351,42 @@ def clip_scale(total_sq, max_norm, scale):
     _check(lib().sbp_clip_scale(float(total_sq), float(max_norm), float(scale),
                                 ctypes.byref(out), ctypes.byref(coef)))
     return out.value, coef.value
+
+
+def unpack_params(plan, flat, params, bucket=-1, stream=None):
+    """sbp_unpack_params: flat bf16 buckets -> per-tensor bf16 parameters.
+
+    params: one 2-byte device tensor per plan tensor (None allowed outside the
+    selected bucket)."""
+    if len(params) != plan.num_tensors:
+        raise ValueError("unpack_params: one parameter per plan tensor")
+    if flat.numel() != plan.flat_numel:
+        raise ValueError("unpack_params: flat has the wrong size")
+    arr = (ctypes.c_void_p * max(len(params), 1))()
+    for t, p in enumerate(params):
+        if p is None:
+            continue
+        if p.numel() != plan.numels[t]:
+            raise ValueError(f"unpack_params: tensor {t} has {p.numel()} elements")
+        if p.numel():
+            arr[t] = _dev(p, 2, "unpack_params params")
+    _check(lib().sbp_unpack_params(plan.handle, int(bucket), _dev(flat, 2, "unpack_params flat"),
+                                   arr, _stream(stream, flat)))
+
+
+def shard_of(plan, rank, flat, shard, bucket=-1, stream=None):
+    """sbp_shard_of: rank's chunk of every bucket of `flat` -> shard layout."""
+    if flat.numel() != plan.flat_numel or shard.numel() != plan.shard_numel:
+        raise ValueError("shard_of: flat or shard has the wrong size")
+    _check(lib().sbp_shard_of(plan.handle, int(bucket), int(rank), _dev(flat, 2, "shard_of flat"),
+                              _dev(shard, 2, "shard_of shard"), _stream(stream, flat)))
+
+
+def gather_shards(plan, shards, flat, bucket=-1, stream=None):
+    """sbp_gather_shards: the N ranks' shards -> flat bucket layout (all-gather layout)."""
+    if len(shards) != plan.world_n:
+        raise ValueError("gather_shards: one shard per rank")
+    if flat.numel() != plan.flat_numel or any(s.numel() != plan.shard_numel for s in shards):
+        raise ValueError("gather_shards: flat or a shard has the wrong size")
+    _check(lib().sbp_gather_shards(plan.handle, int(bucket), _ptrs(shards, "gather_shards shards"),
+                                   _dev(flat, 2, "gather_shards flat"), _stream(stream, flat)))

@@ -34,13 +34,24 @@ struct Bucket {
 
 }  // namespace sbp
 
+struct sbp_plan;
+
+namespace sbp {
+// plan.cpp: fixed-size split plan, and the per-tensor flat positions.
+sbp_status split_plan(sbp_plan* p, int64_t cap_bytes, bool reverse);
+void finish_flat_positions(sbp_plan* p);
+}  // namespace sbp
+
 struct sbp_plan {
   std::vector<int64_t> numel;
-  std::vector<int32_t> tensor_bucket;
-  std::vector<int64_t> tensor_offset;
+  std::vector<int32_t> tensor_bucket;  // bucket of the tensor's first element
+  std::vector<int64_t> tensor_offset;  // offset of that element in the bucket
+  std::vector<int64_t> tensor_flat;    // position of the tensor in the flat buffer
+  std::vector<int32_t> flat_order;     // non-empty tensors by flat position
   std::vector<sbp::Bucket> buckets;
   int32_t world_n;
   int32_t align;
+  bool split;                          // fixed-size buckets, tensors may straddle
   int64_t shard_numel;
   int64_t flat_numel;
 };

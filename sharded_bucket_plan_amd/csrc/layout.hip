@@ -1,0 +1,318 @@
+// Layout moves between per-tensor buffers, flat buckets and shards:
+//   pack    per-tensor bf16 gradients -> flat buckets (+0 elsewhere)
+//   unpack  flat buckets -> per-tensor bf16 parameters (the all-gather side)
+//   shard_of  one rank's chunk of every bucket -> its shard layout (what that
+//             rank contributes to each owner in the reduce-scatter)
+//   gather    the N ranks' shards -> flat buckets (what the all-gather
+//             assembles on every rank)
+// ("Parallelisms" (vladislavkruglikov.com), Gradient bucketing: gradients
+// gathered into buffers at fixed offsets; FSDP / Flat parameter: one
+// contiguous buffer concatenating parameters, the originals being views into
+// it; YaFSDP writes gradients straight into communication buffers, which is
+// what the bucket here is: a persistent, caller-owned buffer written in place;
+// ZeRO-1: reduce-scatter to owners, all-gather of the updated shards.)
+//
+// Design (CDNA4).  Every call is a list of copy segments (source, destination,
+// length; a null source writes zeros), cut into equal chunks of 2048
+// elements rather than per tensor, because a bucket mixes 4096-element norm
+// vectors with matrices of half a billion elements:
+//   - up to kMaxSegs segments travel by value in the kernel arguments (no
+//     device allocation, nothing to upload, so the calls can be captured in a
+//     graph); longer lists take several launches;
+//   - one pass: one block per chunk, in XCD-contiguous order (the order the
+//     streaming kernels use); a block finds its segment by binary search over
+//     the chunk starts, uniform per block, so it runs on scalar loads of the
+//     kernel arguments;
+//   - a chunk is 256 lanes x 16 bytes, fully coalesced, when source and
+//     destination are 16-byte aligned; otherwise element by element.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+#ifndef SBP_PACK_ROUNDS
+#define SBP_PACK_ROUNDS 1
+#endif
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kRounds = SBP_PACK_ROUNDS;
+constexpr int kXcds = 8;
+constexpr int64_t kChunk = static_cast<int64_t>(kBlock) * 8 * kRounds;  // elements
+constexpr int kMaxSegs = 96;
+
+struct Seg {
+  const uint16_t* src;  // null: zero fill
+  uint16_t* dst;
+  int64_t len;          // elements
+  int64_t first_chunk;  // chunk index (within this launch) of the segment's start
+};
+
+struct SegList {
+  Seg seg[kMaxSegs];
+  int32_t count;
+  int64_t chunks;  // total chunks of this launch
+};
+
+__device__ __forceinline__ int find_seg(const SegList& L, int64_t c) {
+  int lo = 0, hi = L.count - 1;  // last segment whose first_chunk <= c
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (L.seg[mid].first_chunk <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
+  // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
+  unsigned b = blockIdx.x;
+  const unsigned per = gridDim.x / kXcds;
+  if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+  const int64_t c = b;
+  const Seg sg = L.seg[find_seg(L, c)];
+  const int64_t start = (c - sg.first_chunk) * kChunk;
+  const int64_t rem = sg.len - start;
+  const int64_t cnt = rem < kChunk ? rem : kChunk;
+  uint16_t* d = sg.dst + start;
+  const uint16_t* s = sg.src ? sg.src + start : nullptr;
+  const bool vec = (reinterpret_cast<uintptr_t>(sg.dst) & 15) == 0 &&
+                   (s == nullptr || (reinterpret_cast<uintptr_t>(sg.src) & 15) == 0);
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int64_t e = static_cast<int64_t>(k) * kBlock * 8 + threadIdx.x * 8;
+      if (e + 8 <= cnt) {
+        uint4 x = s ? *reinterpret_cast<const uint4*>(s + e) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(d + e) = x;
+      } else {
+        for (int64_t j = e; j < cnt; ++j) d[j] = s ? s[j] : 0;
+      }
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < cnt; j += kBlock) d[j] = s ? s[j] : 0;
+  }
+}
+
+sbp_status launch_segments(const char* who, const std::vector<Seg>& segs, hipStream_t stream) {
+  (void)hipGetLastError();
+  for (size_t i = 0; i < segs.size(); i += kMaxSegs) {
+    SegList L;
+    L.count = 0;
+    L.chunks = 0;
+    for (size_t j = i; j < segs.size() && j < i + kMaxSegs; ++j) {
+      Seg s = segs[j];
+      s.first_chunk = L.chunks;
+      L.chunks += (s.len + kChunk - 1) / kChunk;
+      L.seg[L.count++] = s;
+    }
+    if (L.chunks > 0x7FFFFFFF)
+      return sbp::fail(SBP_ERANGE, std::string(who) + ": too many chunks for one launch");
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(L.chunks)), dim3(kBlock), 0,
+                       stream, L);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return sbp::fail(SBP_EHIP, std::string(who) + ": launch failed: " + hipGetErrorString(e));
+  }
+  return sbp::ok();
+}
+
+// Flat range [lo, hi) of bucket `bucket` (-1: all buckets).
+sbp_status bucket_range(const char* who, const sbp_plan* plan, int32_t bucket, int32_t* b0,
+                        int32_t* b1, int64_t* lo, int64_t* hi) {
+  const int32_t nb = static_cast<int32_t>(plan->buckets.size());
+  if (bucket < -1 || bucket >= nb)
+    return sbp::fail(SBP_EINVAL, std::string(who) + ": bucket out of range");
+  *b0 = bucket < 0 ? 0 : bucket;
+  *b1 = bucket < 0 ? nb : bucket + 1;
+  if (*b0 >= *b1) {
+    *lo = *hi = 0;
+  } else {
+    *lo = plan->buckets[*b0].flat_offset;
+    *hi = plan->buckets[*b1 - 1].flat_offset + plan->buckets[*b1 - 1].padded;
+  }
+  return SBP_OK;
+}
+
+// Pieces of the non-empty tensors inside flat [lo, hi): (tensor, first
+// element of the tensor in the piece, flat position, length), in flat order.
+struct Piece {
+  int32_t t;
+  int64_t elem, flat, len;
+};
+
+std::vector<Piece> pieces_in(const sbp_plan* plan, int64_t lo, int64_t hi) {
+  std::vector<Piece> out;
+  const auto& order = plan->flat_order;
+  // first tensor that ends after lo
+  auto it = std::lower_bound(order.begin(), order.end(), lo, [&](int32_t t, int64_t x) {
+    return plan->tensor_flat[t] + plan->numel[t] <= x;
+  });
+  for (; it != order.end(); ++it) {
+    const int32_t t = *it;
+    const int64_t a = plan->tensor_flat[t], e = a + plan->numel[t];
+    if (a >= hi) break;
+    const int64_t s = a > lo ? a : lo, f = e < hi ? e : hi;
+    if (f > s) out.push_back(Piece{t, s - a, s, f - s});
+  }
+  return out;
+}
+
+// Device pointers in `ptrs` (lengths in bytes) pairwise disjoint?
+bool disjoint(std::vector<std::pair<uintptr_t, int64_t>> ranges) {
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].first + static_cast<uintptr_t>(ranges[i - 1].second))
+      return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket, const void* const* tensor_grads,
+                          void* flat, hipStream_t stream) {
+  const char* who = "sbp_pack_grads";
+  if (plan == nullptr) return sbp::fail(SBP_EINVAL, "sbp_pack_grads: plan is null");
+  if (tensor_grads == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_pack_grads: tensor_grads is null");
+  if (flat == nullptr) return sbp::fail(SBP_EINVAL, "sbp_pack_grads: flat is null");
+  if (!sbp::aligned(flat, 16))
+    return sbp::fail(SBP_EALIGN, "sbp_pack_grads: flat must be 16-byte aligned");
+  int32_t b0, b1;
+  int64_t lo, hi;
+  sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
+  if (st != SBP_OK) return st;
+  uint16_t* F = static_cast<uint16_t*>(flat);
+  std::vector<Seg> segs;
+  try {
+    int64_t pos = lo;
+    for (const Piece& pc : pieces_in(plan, lo, hi)) {
+      const void* src = tensor_grads[pc.t];
+      if (src == nullptr)
+        return sbp::fail(SBP_EINVAL, "sbp_pack_grads: gradient pointer of a tensor is null");
+      if (!sbp::aligned(src, 2))
+        return sbp::fail(SBP_EALIGN, "sbp_pack_grads: gradients must be 2-byte aligned");
+      if (sbp::overlaps(src, 2 * plan->numel[pc.t], flat, 2 * plan->flat_numel))
+        return sbp::fail(SBP_EINVAL, "sbp_pack_grads: a gradient overlaps the flat buffer");
+      if (pc.flat > pos) segs.push_back(Seg{nullptr, F + pos, pc.flat - pos, 0});
+      segs.push_back(Seg{static_cast<const uint16_t*>(src) + pc.elem, F + pc.flat, pc.len, 0});
+      pos = pc.flat + pc.len;
+    }
+    if (hi > pos) segs.push_back(Seg{nullptr, F + pos, hi - pos, 0});
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_pack_grads: out of host memory");
+  }
+  return launch_segments(who, segs, stream);
+}
+
+sbp_status sbp_unpack_params(const sbp_plan* plan, int32_t bucket, const void* flat,
+                             void* const* tensor_params, hipStream_t stream) {
+  const char* who = "sbp_unpack_params";
+  if (plan == nullptr) return sbp::fail(SBP_EINVAL, "sbp_unpack_params: plan is null");
+  if (tensor_params == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_unpack_params: tensor_params is null");
+  if (flat == nullptr) return sbp::fail(SBP_EINVAL, "sbp_unpack_params: flat is null");
+  if (!sbp::aligned(flat, 16))
+    return sbp::fail(SBP_EALIGN, "sbp_unpack_params: flat must be 16-byte aligned");
+  int32_t b0, b1;
+  int64_t lo, hi;
+  sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
+  if (st != SBP_OK) return st;
+  const uint16_t* F = static_cast<const uint16_t*>(flat);
+  std::vector<Seg> segs;
+  try {
+    std::vector<std::pair<uintptr_t, int64_t>> outs;
+    int32_t last = -1;
+    for (const Piece& pc : pieces_in(plan, lo, hi)) {
+      void* dst = tensor_params[pc.t];
+      if (dst == nullptr)
+        return sbp::fail(SBP_EINVAL, "sbp_unpack_params: parameter pointer of a tensor is null");
+      if (!sbp::aligned(dst, 2))
+        return sbp::fail(SBP_EALIGN, "sbp_unpack_params: parameters must be 2-byte aligned");
+      if (sbp::overlaps(dst, 2 * plan->numel[pc.t], flat, 2 * plan->flat_numel))
+        return sbp::fail(SBP_EINVAL, "sbp_unpack_params: a parameter overlaps the flat buffer");
+      if (pc.t != last)
+        outs.push_back({reinterpret_cast<uintptr_t>(dst), 2 * plan->numel[pc.t]});
+      last = pc.t;
+      segs.push_back(Seg{F + pc.flat, static_cast<uint16_t*>(dst) + pc.elem, pc.len, 0});
+    }
+    if (!disjoint(outs))
+      return sbp::fail(SBP_EINVAL, "sbp_unpack_params: parameter buffers overlap");
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_unpack_params: out of host memory");
+  }
+  return launch_segments(who, segs, stream);
+}
+
+sbp_status sbp_shard_of(const sbp_plan* plan, int32_t bucket, int32_t rank, const void* flat,
+                        void* shard, hipStream_t stream) {
+  const char* who = "sbp_shard_of";
+  if (plan == nullptr || flat == nullptr || shard == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_shard_of: null argument");
+  if (rank < 0 || rank >= plan->world_n)
+    return sbp::fail(SBP_EINVAL, "sbp_shard_of: rank out of range");
+  if (!sbp::aligned(flat, 16) || !sbp::aligned(shard, 16))
+    return sbp::fail(SBP_EALIGN, "sbp_shard_of: buffers must be 16-byte aligned");
+  if (sbp::overlaps(flat, 2 * plan->flat_numel, shard, 2 * plan->shard_numel))
+    return sbp::fail(SBP_EINVAL, "sbp_shard_of: the shard overlaps the flat buffer");
+  int32_t b0, b1;
+  int64_t lo, hi;
+  sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
+  if (st != SBP_OK) return st;
+  const uint16_t* F = static_cast<const uint16_t*>(flat);
+  uint16_t* S = static_cast<uint16_t*>(shard);
+  std::vector<Seg> segs;
+  try {
+    for (int32_t b = b0; b < b1; ++b) {
+      const sbp::Bucket& k = plan->buckets[b];
+      if (k.chunk > 0)
+        segs.push_back(Seg{F + k.flat_offset + rank * k.chunk, S + k.shard_offset, k.chunk, 0});
+    }
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_shard_of: out of host memory");
+  }
+  return launch_segments(who, segs, stream);
+}
+
+sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                             void* flat, hipStream_t stream) {
+  const char* who = "sbp_gather_shards";
+  if (plan == nullptr || shards == nullptr || flat == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_gather_shards: null argument");
+  if (!sbp::aligned(flat, 16))
+    return sbp::fail(SBP_EALIGN, "sbp_gather_shards: flat must be 16-byte aligned");
+  for (int32_t s = 0; s < plan->world_n; ++s) {
+    if (shards[s] == nullptr) return sbp::fail(SBP_EINVAL, "sbp_gather_shards: a shard is null");
+    if (!sbp::aligned(shards[s], 16))
+      return sbp::fail(SBP_EALIGN, "sbp_gather_shards: shards must be 16-byte aligned");
+    if (sbp::overlaps(shards[s], 2 * plan->shard_numel, flat, 2 * plan->flat_numel))
+      return sbp::fail(SBP_EINVAL, "sbp_gather_shards: a shard overlaps the flat buffer");
+  }
+  int32_t b0, b1;
+  int64_t lo, hi;
+  sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
+  if (st != SBP_OK) return st;
+  uint16_t* F = static_cast<uint16_t*>(flat);
+  std::vector<Seg> segs;
+  try {
+    for (int32_t b = b0; b < b1; ++b) {
+      const sbp::Bucket& k = plan->buckets[b];
+      if (k.chunk == 0) continue;
+      for (int32_t s = 0; s < plan->world_n; ++s)
+        segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + k.shard_offset,
+                           F + k.flat_offset + s * k.chunk, k.chunk, 0});
+    }
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_gather_shards: out of host memory");
+  }
+  return launch_segments(who, segs, stream);
+}
+
+}  // extern "C"

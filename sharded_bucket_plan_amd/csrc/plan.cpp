@@ -10,8 +10,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -47,6 +49,85 @@ int64_t round_up(int64_t x, int64_t m) {
 }
 
 }  // namespace
+
+// Flat position of every tensor, and the non-empty tensors in flat order.
+void finish_flat_positions(sbp_plan* p) {
+  const int32_t T = static_cast<int32_t>(p->numel.size());
+  p->tensor_flat.assign(T, 0);
+  for (int32_t t = 0; t < T; ++t)
+    p->tensor_flat[t] = p->buckets.empty()
+                            ? 0
+                            : p->buckets[p->tensor_bucket[t]].flat_offset + p->tensor_offset[t];
+  p->flat_order.clear();
+  for (int32_t t = 0; t < T; ++t)
+    if (p->numel[t] > 0) p->flat_order.push_back(t);
+  std::sort(p->flat_order.begin(), p->flat_order.end(),
+            [&](int32_t a, int32_t b) { return p->tensor_flat[a] < p->tensor_flat[b]; });
+}
+
+// Fixed-size buckets over the concatenated tensors: the flat buffer (each
+// tensor at the first multiple of align after the previous one, in visit
+// order) is cut into buckets of cap/2 elements rounded down to a multiple of
+// align*N (at least align*N); tensors may straddle buckets and only the last
+// bucket can be short (then padded to align*N).  Flat parameters cut into
+// equal communication pieces ("Parallelisms", FSDP / Flat parameter).
+sbp_status split_plan(sbp_plan* p, int64_t cap_bytes, bool reverse) {
+  const int32_t T = static_cast<int32_t>(p->numel.size());
+  const int64_t unit = static_cast<int64_t>(p->align) * p->world_n;
+  int64_t size = (cap_bytes / 2) / unit * unit;
+  if (size < unit) size = unit;
+  std::vector<int64_t> pos(T, 0);
+  int64_t end = 0;
+  for (int32_t i = 0; i < T; ++i) {
+    const int32_t t = reverse ? T - 1 - i : i;
+    const int64_t start = end == 0 ? 0 : round_up(end, p->align);
+    int64_t e;
+    if (start < 0 || !add_ok(start, p->numel[t], &e))
+      return fail(SBP_ERANGE, "sbp_bucket_plan: flat size overflows");
+    pos[t] = start;
+    end = e;
+  }
+  const int64_t nb = end > 0 ? (end + size - 1) / size : (T > 0 ? 1 : 0);
+  if (nb > INT32_MAX) return fail(SBP_ERANGE, "sbp_bucket_plan: too many buckets");
+  p->tensor_bucket.assign(T, 0);
+  p->tensor_offset.assign(T, 0);
+  for (int32_t t = 0; t < T; ++t) {
+    int64_t b = pos[t] / size;
+    if (b > nb - 1) b = nb - 1;
+    p->tensor_bucket[t] = static_cast<int32_t>(b);
+    p->tensor_offset[t] = pos[t] - b * size;
+  }
+  p->buckets.assign(static_cast<size_t>(nb), Bucket{{}, 0, 0, 0, 0, 0});
+  int64_t shard = 0, flat = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    Bucket& k = p->buckets[b];
+    const int64_t lo = b * size, hi = lo + size;
+    k.used = (end < hi ? end : hi) - lo;
+    if (k.used < 0) k.used = 0;
+    k.padded = round_up(k.used, unit);
+    if (k.padded < 0) return fail(SBP_ERANGE, "sbp_bucket_plan: padding overflows");
+    k.chunk = k.padded / p->world_n;
+    k.shard_offset = shard;
+    k.flat_offset = lo;
+    shard += k.chunk;
+    flat += k.padded;
+  }
+  // members of each bucket, in visit order
+  for (int32_t i = 0; i < T; ++i) {
+    const int32_t t = reverse ? T - 1 - i : i;
+    if (p->numel[t] == 0) {
+      p->buckets[p->tensor_bucket[t]].tensors.push_back(t);
+      continue;
+    }
+    const int64_t b0 = pos[t] / size, b1 = (pos[t] + p->numel[t] - 1) / size;
+    for (int64_t b = b0; b <= b1; ++b) p->buckets[b].tensors.push_back(t);
+  }
+  p->shard_numel = shard;
+  p->flat_numel = flat;
+  finish_flat_positions(p);
+  return SBP_OK;
+}
+
 }  // namespace sbp
 
 using sbp::fail;
@@ -72,7 +153,7 @@ sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
   if (world_n <= 0) return fail(SBP_EINVAL, "sbp_bucket_plan: world_n must be > 0");
   if (align_elems <= 0 || align_elems > 4096 || (align_elems & (align_elems - 1)))
     return fail(SBP_EINVAL, "sbp_bucket_plan: align_elems must be a power of two in 1..4096");
-  if (flags != SBP_ORDER_REVERSE && flags != SBP_ORDER_FORWARD)
+  if (flags & ~(SBP_ORDER_FORWARD | SBP_SPLIT_TENSORS))
     return fail(SBP_EINVAL, "sbp_bucket_plan: unknown flags");
   for (int32_t t = 0; t < n_tensors; ++t)
     if (numel[t] < 0) return fail(SBP_EINVAL, "sbp_bucket_plan: negative numel");
@@ -85,8 +166,18 @@ sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
     p->tensor_offset.assign(n_tensors, 0);
     p->world_n = world_n;
     p->align = align_elems;
+    p->split = (flags & SBP_SPLIT_TENSORS) != 0;
+    const bool reverse = (flags & SBP_ORDER_FORWARD) == 0;
+    if (p->split) {
+      sbp_status st = sbp::split_plan(p, bucket_cap_bytes, reverse);
+      if (st != SBP_OK) {
+        delete p;
+        return st;
+      }
+      *out = p;
+      return ok();
+    }
 
-    const bool reverse = (flags == SBP_ORDER_REVERSE);
     sbp::Bucket cur{{}, 0, 0, 0, 0, 0};
     auto close = [&]() { p->buckets.push_back(cur); cur = sbp::Bucket{{}, 0, 0, 0, 0, 0}; };
     for (int32_t i = 0; i < n_tensors; ++i) {
@@ -120,6 +211,7 @@ sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
     }
     p->shard_numel = shard;
     p->flat_numel = flat;
+    sbp::finish_flat_positions(p);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(SBP_ENOMEM, "sbp_bucket_plan: out of host memory");

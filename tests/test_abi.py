@@ -204,3 +204,54 @@ def test_grad_sq_norm_validates_before_launch():
     assert f(peers, 2, None, 1.0, n, V(0x100000), ws, need, sq, None) == sbp.SBP_EINVAL
     assert f(peers, 2, None, 1.0, n, None, ws, need, V(0x800000), None) == sbp.SBP_EINVAL
     assert f(peers, 2, None, 1.0, -1, None, ws, need, sq, None) == sbp.SBP_EINVAL
+
+
+def _same_split_plan(numels, cap, N, align=8, order="reverse"):
+    p = sbp.bucket_plan(numels, cap, N, align, order, split=True)
+    o = OP.bucket_plan(numels, cap, N, align, order, split=True)
+    assert p.num_buckets == len(o.buckets)
+    assert p.shard_numel == o.shard_numel and p.flat_numel == o.flat_numel
+    for b, ob in enumerate(o.buckets):
+        assert p.bucket(b) == dict(used=ob.used, padded=ob.padded, chunk=ob.chunk,
+                                   shard_offset=ob.shard_offset, flat_offset=ob.flat_offset)
+        assert p.bucket_tensors(b) == ob.tensors
+    for t in range(len(numels)):
+        assert p.tensor(t) == (o.tensor_bucket[t], o.tensor_offset[t])
+
+
+def test_split_plan_matches_oracle():
+    rng = random.Random(5)
+    for _ in range(400):
+        T = rng.randint(0, 10)
+        numels = [rng.choice([0, 1, 3, 7, 8, 9, 17, 64, 100, 1000]) for _ in range(T)]
+        _same_split_plan(numels, rng.randint(1, 3000), rng.choice([1, 2, 3, 4, 8]),
+                         rng.choice([1, 2, 4, 8, 16]), rng.choice(["reverse", "forward"]))
+    w = synth.WORKLOADS["gpt_7b5"]
+    for mib in (1, 25, 256):
+        _same_split_plan(w.numels, mib << 20, w.world_n)
+    for name in ("tiny_mlp", "gpt2_small"):
+        w = synth.WORKLOADS[name]
+        _same_split_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+
+
+def test_layout_calls_validate_before_launch():
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    plan = sbp.bucket_plan([10, 20], 1 << 20, 2)
+    two = (V * 2)(0x100000, 0x200000)
+    assert L.sbp_unpack_params(None, -1, V(0x300000), two, None) == sbp.SBP_EINVAL
+    assert L.sbp_unpack_params(plan.handle, -1, V(0x300008), two, None) == sbp.SBP_EALIGN
+    assert L.sbp_unpack_params(plan.handle, 3, V(0x300000), two, None) == sbp.SBP_EINVAL
+    assert L.sbp_unpack_params(plan.handle, -1, V(0x300000), (V * 2)(0x100001, 0x200000),
+                               None) == sbp.SBP_EALIGN
+    assert L.sbp_unpack_params(plan.handle, -1, V(0x300000), (V * 2)(0x100000, 0x100010),
+                               None) == sbp.SBP_EINVAL  # the two outputs overlap
+    assert L.sbp_unpack_params(plan.handle, -1, V(0x100000), two, None) == sbp.SBP_EINVAL
+    assert L.sbp_shard_of(plan.handle, -1, 2, V(0x300000), V(0x400000), None) == sbp.SBP_EINVAL
+    assert L.sbp_shard_of(plan.handle, -1, 0, V(0x300000), V(0x400008), None) == sbp.SBP_EALIGN
+    assert L.sbp_shard_of(plan.handle, -1, 0, V(0x300000), V(0x300010), None) == sbp.SBP_EINVAL
+    assert L.sbp_gather_shards(plan.handle, -1, (V * 2)(0x100000, None), V(0x300000),
+                               None) == sbp.SBP_EINVAL
+    assert L.sbp_gather_shards(plan.handle, -1, two, V(0x100000), None) == sbp.SBP_EINVAL
+    assert L.sbp_gather_shards(plan.handle, -1, (V * 2)(0x100004, 0x200000), V(0x300000),
+                               None) == sbp.SBP_EALIGN

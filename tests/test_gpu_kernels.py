@@ -332,3 +332,68 @@ def test_clipped_step_two_shards(max_norm):
         want = OS.shard_step([], Gh[s], want_cs, th, m, v, hp, 1)
         got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
         assert H.assert_state_close(got, want, f"clipped shard {s}") == 0
+
+
+# ---- layout moves: pack / unpack / shard_of / gather on both plan kinds ---------
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("misalign", [False, True])
+def test_layout_moves(split, misalign):
+    import torch
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
+    N = 4
+    pl = sbp.bucket_plan(numels, 600, N, split=split)
+    opl = OP.bucket_plan(numels, 600, N, split=split)
+    grads_h = [synth.normal_bf16(31, synth.tensor_stream(1, 0, 0, t), n, 1e-2)
+               for t, n in enumerate(numels)]
+    keep = []
+
+    def dev_tensor(h):
+        if misalign and h.size:
+            base = torch.empty(h.size + 5, dtype=torch.int16, device=H.dev())
+            keep.append(base)
+            v = base[5:]
+            v.copy_(H.from_np_u16(h))
+            return v
+        return H.from_np_u16(h) if h.size else H.empty_u16(0)
+
+    gd = [dev_tensor(h) for h in grads_h]
+    flat = H.empty_u16(pl.flat_numel)
+    flat.fill_(0x7777)
+    sbp.pack_grads(pl, gd, flat)
+    want_flat = OS.pack(opl, grads_h)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(flat), want_flat, "pack")
+    # per-bucket pack of a second buffer
+    flat2 = H.empty_u16(pl.flat_numel)
+    flat2.fill_(0x7777)
+    for b in range(pl.num_buckets):
+        members = set(pl.bucket_tensors(b))
+        sbp.pack_grads(pl, [gd[t] if t in members else None for t in range(len(numels))],
+                       flat2, bucket=b)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(flat2), want_flat, "pack by bucket")
+    # shard_of each rank, then gather back
+    shards = [H.empty_u16(pl.shard_numel) for _ in range(N)]
+    for s in range(N):
+        sbp.shard_of(pl, s, flat, shards[s])
+    torch.cuda.synchronize()
+    for s in range(N):
+        H.assert_bits_equal(H.to_np_u16(shards[s]), OS.chunk(opl, want_flat, s), f"shard {s}")
+    back = H.empty_u16(pl.flat_numel)
+    back.fill_(0x1234)
+    sbp.gather_shards(pl, shards, back)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(back), want_flat, "gather")
+    # unpack into per-tensor buffers (all at once, and bucket by bucket)
+    outs = [dev_tensor(np.zeros(n, np.uint16)) for n in numels]
+    sbp.unpack_params(pl, back, outs)
+    outs2 = [dev_tensor(np.zeros(n, np.uint16)) for n in numels]
+    for b in range(pl.num_buckets):
+        members = set(pl.bucket_tensors(b))
+        sbp.unpack_params(pl, back, [outs2[t] if t in members else None
+                                     for t in range(len(numels))], bucket=b)
+    torch.cuda.synchronize()
+    for t, h in enumerate(grads_h):
+        H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack tensor {t}")
+        H.assert_bits_equal(H.to_np_u16(outs2[t]), h, f"unpack by bucket, tensor {t}")

@@ -31,18 +31,6 @@ def _hp(w):
     return sbp.AdamW(w.adamw.lr, w.adamw.beta1, w.adamw.beta2, w.adamw.eps, w.adamw.weight_decay)
 
 
-def _chunk_dev(plan, flat, s):
-    """Rank s's share of a device flat buffer (what the reduce-scatter would
-    deliver from that rank; a plain gather of slices, not part of the path)."""
-    import torch
-    parts = []
-    for b in range(plan.num_buckets):
-        info = plan.bucket(b)
-        o = info["flat_offset"] + s * info["chunk"]
-        parts.append(flat[o:o + info["chunk"]])
-    return torch.cat(parts).contiguous()
-
-
 @pytest.mark.parametrize("s", [0, 1])
 def test_tiny_mlp_all_steps(s):
     """2-layer MLP, N=2, R=2: each rank packs its per-tensor gradients, this
@@ -59,6 +47,7 @@ def test_tiny_mlp_all_steps(s):
     dp = H.empty_u16(n)
     flats = [H.empty_u16(pl.flat_numel) for _ in range(w.R)]
     grads = [[H.empty_u16(k) for k in w.numels] for _ in range(w.R)]
+    peers = [H.empty_u16(n) for _ in range(w.R)]
     want = (th, z, z, None)
     for t in range(1, w.steps + 1):
         host_flats = []
@@ -70,7 +59,8 @@ def test_tiny_mlp_all_steps(s):
                 gh.append(synth.normal_bf16(SEED, st, k, w.grad_sigma))
             sbp.pack_grads(pl, grads[r], flats[r])
             host_flats.append(OS.pack(opl, gh))
-        peers = [_chunk_dev(pl, f, s) for f in flats]
+        for r in range(w.R):  # rank r's contribution to this rank's shard
+            sbp.shard_of(pl, s, flats[r], peers[r])
         scale = sbp.mean_scale(w.R)
         sbp.adamw_shard(peers, None, scale, dth, dm, dv, dp, hp, t)
         want = OS.shard_step([OS.chunk(opl, f, s) for f in host_flats], None,
@@ -258,3 +248,56 @@ def test_llama3_8b_dp_pack_and_step_sampled():
     got = _sampled_state(dth, dm, dv, dp, idx)
     for a, b, name in zip(got, want, ("master", "m", "v", "param")):
         H.assert_bits_equal(a, b, f"llama3_8b_dp {name}")
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_tiny_mlp_zero_round_trip(split):
+    """Both ranks of the 2-layer MLP on one GPU, each step: every rank packs its
+    per-tensor gradients, each owner takes its chunk of every rank's buckets
+    (shard_of), reduces and updates its shard, the bf16 shards are gathered
+    and unpacked into per-tensor parameters -- the reduce-scatter / update /
+    all-gather round trip, all in the library's kernels, against the oracle."""
+    import torch
+    w = synth.WORKLOADS["tiny_mlp"]
+    hp = _hp(w)
+    cap = w.bucket_cap_bytes if not split else 256 << 10  # several split buckets
+    pl = sbp.bucket_plan(w.numels, cap, w.world_n, split=split)
+    opl = OP.bucket_plan(w.numels, cap, w.world_n, split=split)
+    N, R, n = w.world_n, w.R, pl.shard_numel
+    state = []
+    ostate = []
+    for s in range(N):
+        th = synth.normal_f32(SEED, synth.master_stream(s), n, w.master_sigma)
+        z = np.zeros(n, np.float32)
+        state.append([H.from_np_f32(th), H.from_np_f32(z), H.from_np_f32(z), H.empty_u16(n)])
+        ostate.append((th, z, z))
+    grads = [[H.empty_u16(k) for k in w.numels] for _ in range(R)]
+    flats = [H.empty_u16(pl.flat_numel) for _ in range(R)]
+    recv = [[H.empty_u16(n) for _ in range(R)] for _ in range(N)]
+    gathered = H.empty_u16(pl.flat_numel)
+    params = [H.empty_u16(k) for k in w.numels]
+    for t in range(1, 4):
+        host_flats = []
+        for r in range(R):
+            gh = []
+            for tid, k in enumerate(w.numels):
+                st = synth.tensor_stream(t, 0, r, tid)
+                synth.dev_normal_bf16(grads[r][tid], SEED, st, w.grad_sigma)
+                gh.append(synth.normal_bf16(SEED, st, k, w.grad_sigma))
+            sbp.pack_grads(pl, grads[r], flats[r])
+            host_flats.append(OS.pack(opl, gh))
+        oshards = []
+        for s in range(N):
+            for r in range(R):
+                sbp.shard_of(pl, s, flats[r], recv[s][r])
+            sbp.adamw_shard(recv[s], None, sbp.mean_scale(R), *state[s][:3], state[s][3], hp, t)
+            th, m, v, p = OS.shard_step([OS.chunk(opl, f, s) for f in host_flats], None,
+                                        OS.mean_scale(R), *ostate[s], hp, t)
+            ostate[s] = (th, m, v)
+            oshards.append(p)
+        sbp.gather_shards(pl, [state[s][3] for s in range(N)], gathered)
+        sbp.unpack_params(pl, gathered, params)
+        torch.cuda.synchronize()
+        want = OS.unpack(opl, OS.gather(opl, oshards))
+        for tid in range(len(w.numels)):
+            H.assert_bits_equal(H.to_np_u16(params[tid]), want[tid], f"step {t} tensor {tid}")
