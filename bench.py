@@ -355,6 +355,78 @@ def cpu_baseline(workload_name, seed, target_s):
                        f"{spent:.1f} s")}
 
 
+def bucket_sweep(seed, reps=5):
+    """Bucket-size sweep on the "7.5B" shard (n = 103,890,048, R = 8): one later
+    microbatch accumulated bucket by bucket -- one launch per bucket, as each
+    bucket's reduce-scatter share arrives -- for caps of 1..256 MiB, with
+    whole-tensor and split-tensor plans.  The per-bucket launches of one pass
+    are captured in a HIP graph and replayed, so host launch cost is left out.
+    Fits the alpha-beta model of "Parallelisms" (Gradient bucketing):
+    T(K buckets) = K * alpha + beta * M, M = (2R + 8) * n bytes."""
+    import numpy as np
+    import torch
+    import sharded_bucket_plan_amd as sbp
+    import synth
+
+    w = synth.WORKLOADS["gpt_7b5"]
+    dev = torch.device("cuda:0")
+    n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+    peers = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
+                                   synth.peer_stream(1, 1, r), w.grad_sigma) for r in range(w.R)]
+    acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    M = (2 * w.R + 8) * n
+    rows = []
+    for split in (False, True):
+        for cap in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+            pl = sbp.bucket_plan(w.numels, cap << 20, w.world_n, split=split)
+            if pl.shard_numel != n:
+                raise SystemExit("bucket sweep: shard size changed with the cap")
+            views = []
+            for b in range(pl.num_buckets):
+                info = pl.bucket(b)
+                o, c = info["shard_offset"], info["chunk"]
+                views.append((acc[o:o + c], [x[o:o + c] for x in peers]))
+
+            def one_pass():
+                for a, ps in views:
+                    sbp.accumulate_grads(a, ps, first=False)
+
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                one_pass()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_pass()
+            g.replay()
+            torch.cuda.synchronize()
+            ms = []
+            for _ in range(reps):
+                a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b2.record()
+                torch.cuda.synchronize()
+                ms.append(a.elapsed_time(b2))
+            med = sorted(ms)[len(ms) // 2]
+            rows.append({"split": split, "cap_MiB": cap, "buckets": pl.num_buckets, "ms": med,
+                         "gbs": M / (med * 1e-3) / 1e9})
+            log(f"bucket sweep: split={split} cap={cap} MiB buckets={pl.num_buckets} "
+                f"{med:.3f} ms {M / (med * 1e-3) / 1e9:.0f} GB/s")
+            del g, views
+    fit = {}
+    for split in (False, True):
+        K = np.array([r["buckets"] for r in rows if r["split"] == split], dtype=np.float64)
+        T = np.array([r["ms"] for r in rows if r["split"] == split], dtype=np.float64)
+        alpha, c = np.polyfit(K, T, 1)
+        fit["split" if split else "whole_tensor"] = {
+            "alpha_us_per_bucket": alpha * 1e3, "beta_M_ms": c,
+            "bandwidth_gbs_at_one_bucket": M / (c * 1e-3) / 1e9}
+    return {"bucket_sweep": rows, "fit": fit, "bytes_per_pass": M, "shard_numel": n}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +439,8 @@ def main():
                     help="add global gradient-norm clipping to the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--bucket-sweep", action="store_true",
+                    help="only run the bucket-size sweep (7.5B shard) and print its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5,
@@ -390,6 +464,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.bucket_sweep:
+        print(json.dumps(bucket_sweep(seed)), flush=True)
+        return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
                           "bytes_each_way": COPY_BYTES, "calls": CALIBRATION_CALLS}))

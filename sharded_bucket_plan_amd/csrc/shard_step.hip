@@ -37,8 +37,10 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <set>
 #include <string>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -437,16 +439,26 @@ Launch launch_for(int64_t n, int lane_bytes) {
   return L;
 }
 
-// Large dynamic LDS needs the kernel's limit raised (idempotent, cheap).
+// Large dynamic LDS needs the kernel's limit raised.  A kernel always asks
+// for the same reservation on a given device (it depends on its bytes per
+// lane and the device's LDS), so this is done once per kernel and device and
+// later launches -- also inside a captured graph -- only enqueue.
 template <typename K>
 sbp_status allow_lds(K kernel, unsigned lds) {
   if (lds <= 65536) return SBP_OK;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const void* key = reinterpret_cast<const void*>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({key, dev})) return SBP_OK;
+  hipError_t e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess)
     return sbp::fail(SBP_EHIP,
                      std::string("raising the kernel's LDS limit failed: ") + hipGetErrorString(e));
+  done.insert({key, dev});
   return SBP_OK;
 }
 

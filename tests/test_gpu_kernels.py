@@ -397,3 +397,62 @@ def test_layout_moves(split, misalign):
     for t, h in enumerate(grads_h):
         H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack tensor {t}")
         H.assert_bits_equal(H.to_np_u16(outs2[t]), h, f"unpack by bucket, tensor {t}")
+
+
+def test_graph_capture_replays():
+    """The calls allocate nothing and pass their tables by value, so a step can
+    be captured in a HIP graph.  Each replay starts from the same saved state
+    (restored by eager copies between replays) and must equal the eager run."""
+    import torch
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
+    pl = sbp.bucket_plan(numels, 600, 1)
+    n = pl.shard_numel
+    R = 2
+    grads = [H.from_np_u16(synth.normal_bf16(41, synth.tensor_stream(1, 0, 0, t), k, 1e-2))
+             if k else H.empty_u16(0) for t, k in enumerate(numels)]
+    flat = H.empty_u16(n)
+    other = H.from_np_u16(synth.normal_bf16(41, synth.peer_stream(1, 0, 1), n, 1e-2))
+    mb0 = [H.from_np_u16(synth.normal_bf16(41, synth.peer_stream(1, 1, r), n, 1e-2))
+           for r in range(R)]
+    th0 = synth.normal_f32(41, synth.master_stream(0), n, 0.02)
+    init = [H.from_np_f32(th0), H.from_np_f32(np.zeros(n, np.float32)),
+            H.from_np_f32(np.zeros(n, np.float32))]
+    work = [x.clone() for x in init]
+    acc = torch.empty(n, dtype=torch.float32, device=H.dev())
+    gsum = torch.empty(n, dtype=torch.float32, device=H.dev())
+    p = H.empty_u16(n)
+    ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=H.dev())
+    sq = torch.empty(1, dtype=torch.float64, device=H.dev())
+    scale = sbp.mean_scale(R, 2)
+
+    def step():
+        sbp.pack_grads(pl, grads, flat)
+        sbp.accumulate_grads(acc, mb0, first=True)
+        sbp.grad_sq_norm([flat, other], acc, scale, n, g_sum_out=gsum, workspace=ws, sq_out=sq)
+        sbp.adamw_shard([], gsum, scale, *work, p, HP, 1)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in work] + [p.clone(), sq.clone()]
+    for x, y in zip(work, init):
+        x.copy_(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the side stream, as capture expects
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for x, y in zip(work, init):
+            x.copy_(y)
+        p.fill_(0)
+        sq.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x for x in work] + [p, sq]
+        for a, b, name in zip(got, eager, ("master", "m", "v", "param", "sq")):
+            assert torch.equal(a, b), f"graph replay differs in {name}"
