@@ -24,6 +24,7 @@ Readings where the pages are silent:
     concatenated in bucket order.
 """
 
+import math
 from dataclasses import dataclass
 
 
@@ -137,6 +138,41 @@ def _split_plan(numels, cap_bytes, world_n, align, order, visit):
     flat = sum(b.padded for b in buckets)
     return Plan([int(x) for x in numels], cap_bytes, world_n, align, order, tensor_bucket,
                 tensor_offset, buckets, shard_off, flat)
+
+
+def per_tensor_plan(numels, world_n, rows=None, align=8, order="reverse"):
+    """One bucket per tensor, each rank owning whole rows of it.
+
+    "Parallelisms", section FSDP: FSDP2 shards each parameter in place
+    (dim 0), keeping parameter identities instead of a flat parameter.  Here
+    tensor t (visit order as before) is its own bucket, padded to a multiple
+    of N * unit_t with unit_t = lcm(align, row_t), row_t = elements per dim-0
+    row (1 for a 1-D view); so every rank's chunk is ceil(numel / (N unit_t))
+    * unit_t elements: whole rows, aligned.
+    """
+    if world_n <= 0 or align <= 0 or (align & (align - 1)):
+        raise ValueError("world_n > 0 and align a power of two required")
+    T = len(numels)
+    rows = [1] * T if rows is None else [int(r) for r in rows]
+    if len(rows) != T or any(r <= 0 for r in rows):
+        raise ValueError("one positive row size per tensor")
+    if any(int(n) < 0 or int(n) % r for n, r in zip(numels, rows)):
+        raise ValueError("numel must be >= 0 and a multiple of its row size")
+    visit = list(range(T - 1, -1, -1)) if order == "reverse" else list(range(T))
+    buckets = []
+    tensor_bucket = [None] * T
+    tensor_offset = [0] * T
+    shard_off = flat_off = 0
+    for t in visit:
+        unit = align * rows[t] // math.gcd(align, rows[t])
+        padded = _round_up(int(numels[t]), world_n * unit)
+        b = len(buckets)
+        buckets.append(Bucket([t], int(numels[t]), padded, padded // world_n, shard_off, flat_off))
+        tensor_bucket[t] = b
+        shard_off += padded // world_n
+        flat_off += padded
+    return Plan([int(x) for x in numels], 0, world_n, align, order, tensor_bucket, tensor_offset,
+                buckets, shard_off, flat_off)
 
 
 # Bytes per parameter of the model state with bf16 params and grads, an fp32

@@ -5,6 +5,7 @@ rule implies; hand-derived plans of the five workloads check the rule's
 concrete outcome; the pages' byte counts check the state accounting.
 """
 
+import math
 import random
 
 import pytest
@@ -265,3 +266,48 @@ def test_split_plan_gpt_7b5_cap_sweep():
                    256: 50}
     pl = P.bucket_plan(w.numels, 25 << 20, 64, split=True)
     assert pl.shard_numel == 103890048  # same shard size as whole-tensor buckets (no padding)
+
+
+# ---- one bucket per tensor, dim-0 row shards -----------------------------------
+
+def test_per_tensor_plan_rows():
+    # a [10, 3] matrix on N = 4 ranks with align 1: torch.chunk-style dim-0 split
+    # gives ceil(10/4) = 3 rows per rank (the last rank 1 row + 2 padding rows)
+    pl = P.per_tensor_plan([30], 4, rows=[3], align=1)
+    b = pl.buckets[0]
+    assert (b.used, b.padded, b.chunk) == (30, 36, 9)
+    # with align 8: unit lcm(8, 3) = 24 elements (8 rows), chunk = 24
+    pl = P.per_tensor_plan([30], 4, rows=[3], align=8)
+    assert (pl.buckets[0].padded, pl.buckets[0].chunk) == (96, 24)
+    with pytest.raises(ValueError):
+        P.per_tensor_plan([31], 4, rows=[3])
+
+
+def test_per_tensor_plan_properties():
+    rng = random.Random(3)
+    for _ in range(1000):
+        T = rng.randint(0, 8)
+        rows = [rng.choice([1, 2, 3, 7, 8, 768]) for _ in range(T)]
+        numels = [r * rng.choice([0, 1, 2, 5, 13]) for r in rows]
+        N = rng.choice([1, 2, 3, 8])
+        align = rng.choice([1, 2, 8])
+        order = rng.choice(["reverse", "forward"])
+        pl = P.per_tensor_plan(numels, N, rows, align, order)
+        visit = list(range(T - 1, -1, -1)) if order == "reverse" else list(range(T))
+        assert [b.tensors for b in pl.buckets] == [[t] for t in visit]
+        for b in pl.buckets:
+            t = b.tensors[0]
+            assert b.used == numels[t] and pl.tensor_offset[t] == 0
+            assert b.chunk % rows[t] == 0 and b.chunk % align == 0  # whole, aligned rows
+            assert b.chunk * N == b.padded >= b.used
+            assert b.padded - b.used < N * (align * rows[t] // math.gcd(align, rows[t]))
+        assert pl.flat_numel == N * pl.shard_numel
+
+
+def test_per_tensor_plan_llama_rows():
+    # Llama-3-8B, N = 8: every matrix's dim 0 (4096, 1024, 14336, 128256) is a
+    # multiple of 8 and rows are multiples of 8, so no padding at all
+    w = synth.WORKLOADS["llama3_8b"]
+    rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
+    pl = P.per_tensor_plan(w.numels, 8, rows)
+    assert len(pl.buckets) == 291 and pl.flat_numel == w.psi and pl.shard_numel == w.psi // 8
