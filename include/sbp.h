@@ -122,6 +122,21 @@ sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
                            sbp_plan** out);
 void sbp_plan_free(sbp_plan* plan);
 
+/* One bucket per tensor, every rank owning whole rows of it ("Parallelisms",
+ * FSDP: FSDP2 shards each parameter in place on dim 0, keeping parameter
+ * identities).  Tensor t (visit order per flags: SBP_ORDER_REVERSE or
+ * SBP_ORDER_FORWARD) is its own bucket, padded to a multiple of
+ * world_n * lcm(align_elems, row_elems[t]); rank s's chunk is then
+ * ceil(numel / (N * unit)) * unit elements -- whole rows, aligned.
+ * row_elems: elements per dim-0 row, or null for 1 (a 1-D view); numel[t]
+ * must be a multiple of it.  Queries and every other call work on the
+ * result as on any plan.  Errors: SBP_EINVAL, SBP_ERANGE, SBP_ENOMEM. */
+sbp_status sbp_bucket_plan_per_tensor(const int64_t* numel,
+                                      const int64_t* row_elems,
+                                      int32_t n_tensors, int32_t world_n,
+                                      int32_t align_elems, uint32_t flags,
+                                      sbp_plan** out);
+
 /* Plan queries.  Counts and offsets are in elements. */
 int32_t sbp_plan_num_tensors(const sbp_plan* plan);
 int32_t sbp_plan_num_buckets(const sbp_plan* plan);

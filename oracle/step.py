@@ -211,6 +211,60 @@ def adamw(theta, m, v, g, sc):
     return theta1, m1, v1
 
 
+# ---- parameter groups --------------------------------------------------------------
+
+def shard_groups(plan, s, tensor_group):
+    """Group of every element of rank s's shard: its tensor's group; a padding
+    element takes the group of the element before it in the shard (group 0 at
+    the very start) -- padding stays +0 under any group."""
+    spans = sorted((plan.tensor_flat_offset(t), plan.tensor_flat_offset(t) + n, t)
+                   for t, n in enumerate(plan.numels) if n)
+    flat_group = np.full(plan.flat_numel, -1, dtype=np.int64)
+    for a, e, t in spans:
+        flat_group[a:e] = tensor_group[t]
+    g = chunk(plan, flat_group, s)
+    prev = 0
+    for j in range(g.size):  # plain loop: padding inherits the group before it
+        if g[j] < 0:
+            g[j] = prev
+        prev = g[j]
+    return g.astype(np.int32)
+
+
+def adamw_grouped(theta, m, v, g, sc, step_size, decay):
+    """adamw() with per-element step_size and decay (binary32 arrays)."""
+    theta = np.asarray(theta, dtype=np.float32)
+    m = np.asarray(m, dtype=np.float32)
+    v = np.asarray(v, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    m1 = sc.beta1 * m + sc.omb1 * g
+    v1 = sc.beta2 * v + sc.omb2 * (g * g)
+    d = np.sqrt(v1) * sc.c2 + sc.eps
+    theta1 = theta * decay - step_size * (m1 / d)
+    return theta1, m1, v1
+
+
+def shard_step_grouped(peers, acc, scale, theta, m, v, hp, groups, elem_group, t):
+    """shard_step() with per-group lr and weight decay (betas, eps and t shared).
+
+    groups: list of (lr, weight_decay); elem_group: group of each element.
+    Each group's step size and decay are that group's host scalars (same
+    rules as adamw_scalars); the element takes its group's pair.
+    """
+    if peers:
+        S = reduce_peers(peers)
+        G = S if acc is None else np.asarray(acc, dtype=np.float32) + S
+    else:
+        G = np.asarray(acc, dtype=np.float32)
+    g = normalise(G, scale)
+    per = [adamw_scalars(lr, hp.beta1, hp.beta2, hp.eps, wd, t) for lr, wd in groups]
+    sc = per[0]
+    step_size = np.array([p.step_size for p in per], dtype=np.float32)[elem_group]
+    decay = np.array([p.decay for p in per], dtype=np.float32)[elem_group]
+    theta1, m1, v1 = adamw_grouped(theta, m, v, g, sc, step_size, decay)
+    return theta1, m1, v1, f32_to_bf16(theta1)
+
+
 # ---- global gradient-norm clipping -------------------------------------------------
 
 CLIP_EPS = 1e-6  # added to the norm before dividing (the common convention)

@@ -31,7 +31,7 @@ EXPORTS = (
     "sbp_plan_bucket_tensors", "sbp_plan_state_bytes", "sbp_mean_scale", "sbp_tokens_scale",
     "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
-    "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards",
+    "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards", "sbp_bucket_plan_per_tensor",
 )
 
 
@@ -96,6 +96,9 @@ def lib():
                               ctypes.c_void_p, ctypes.c_void_p], st),
         "sbp_clip_scale": ([ctypes.c_double, ctypes.c_float, ctypes.c_float,
                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)], st),
+        "sbp_bucket_plan_per_tensor": ([_i64p, _i64p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_uint32,
+                                        ctypes.POINTER(ctypes.c_void_p)], st),
         "sbp_unpack_params": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, _vpp,
                                ctypes.c_void_p], st),
         "sbp_shard_of": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -195,6 +198,23 @@ def bucket_plan(numels, bucket_cap_bytes, world_n, align=8, order="reverse", spl
         flags |= SPLIT_TENSORS
     _check(lib().sbp_bucket_plan(arr, len(numels), int(bucket_cap_bytes), int(world_n),
                                  int(align), flags, ctypes.byref(h)))
+    return Plan(h.value, numels)
+
+
+def bucket_plan_per_tensor(numels, world_n, rows=None, align=8, order="reverse"):
+    """sbp_bucket_plan_per_tensor: one bucket per tensor, dim-0 row shards."""
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
+    rarr = None
+    if rows is not None:
+        if len(rows) != len(numels):
+            raise ValueError("bucket_plan_per_tensor: one row size per tensor")
+        rarr = (ctypes.c_int64 * max(len(rows), 1))(*[int(r) for r in rows])
+    flags = ORDER_REVERSE if order == "reverse" else ORDER_FORWARD
+    if order not in ("reverse", "forward"):
+        flags = 0xFF
+    h = ctypes.c_void_p()
+    _check(lib().sbp_bucket_plan_per_tensor(arr, rarr, len(numels), int(world_n), int(align),
+                                            flags, ctypes.byref(h)))
     return Plan(h.value, numels)
 
 

@@ -220,6 +220,75 @@ sbp_status sbp_bucket_plan(const int64_t* numel, int32_t n_tensors,
   return ok();
 }
 
+sbp_status sbp_bucket_plan_per_tensor(const int64_t* numel, const int64_t* row_elems,
+                                      int32_t n_tensors, int32_t world_n, int32_t align_elems,
+                                      uint32_t flags, sbp_plan** out) {
+  if (out == nullptr) return fail(SBP_EINVAL, "sbp_bucket_plan_per_tensor: out is null");
+  *out = nullptr;
+  if (n_tensors < 0) return fail(SBP_EINVAL, "sbp_bucket_plan_per_tensor: n_tensors < 0");
+  if (n_tensors > 0 && numel == nullptr)
+    return fail(SBP_EINVAL, "sbp_bucket_plan_per_tensor: numel is null");
+  if (world_n <= 0) return fail(SBP_EINVAL, "sbp_bucket_plan_per_tensor: world_n must be > 0");
+  if (align_elems <= 0 || align_elems > 4096 || (align_elems & (align_elems - 1)))
+    return fail(SBP_EINVAL,
+                "sbp_bucket_plan_per_tensor: align_elems must be a power of two in 1..4096");
+  if (flags & ~SBP_ORDER_FORWARD)
+    return fail(SBP_EINVAL, "sbp_bucket_plan_per_tensor: unknown flags");
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    const int64_t row = row_elems ? row_elems[t] : 1;
+    if (numel[t] < 0 || row <= 0 || numel[t] % row != 0)
+      return fail(SBP_EINVAL,
+                  "sbp_bucket_plan_per_tensor: numel must be >= 0 and a multiple of its row size");
+  }
+  sbp_plan* p = new (std::nothrow) sbp_plan();
+  if (p == nullptr) return fail(SBP_ENOMEM, "sbp_bucket_plan_per_tensor: out of host memory");
+  try {
+    p->numel.assign(numel, numel + n_tensors);
+    p->tensor_bucket.assign(n_tensors, -1);
+    p->tensor_offset.assign(n_tensors, 0);
+    p->world_n = world_n;
+    p->align = align_elems;
+    p->split = false;
+    const bool reverse = (flags & SBP_ORDER_FORWARD) == 0;
+    int64_t shard = 0, flat = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+      const int32_t t = reverse ? n_tensors - 1 - i : i;
+      const int64_t row = row_elems ? row_elems[t] : 1;
+      // whole, aligned rows per rank: pad to N * lcm(align, row)
+      const int64_t a = align_elems;
+      int64_t g = a, r = row;
+      while (r) { const int64_t q = g % r; g = r; r = q; }
+      const int64_t unit = a / g * row;
+      int64_t step;
+      if (unit <= 0 || __builtin_mul_overflow(unit, static_cast<int64_t>(world_n), &step)) {
+        delete p;
+        return fail(SBP_ERANGE, "sbp_bucket_plan_per_tensor: row unit overflows");
+      }
+      sbp::Bucket k{{t}, numel[t], 0, 0, shard, flat};
+      k.padded = sbp::round_up(numel[t], step);
+      if (k.padded < 0) {
+        delete p;
+        return fail(SBP_ERANGE, "sbp_bucket_plan_per_tensor: padding overflows");
+      }
+      k.chunk = k.padded / world_n;
+      p->tensor_bucket[t] = static_cast<int32_t>(p->buckets.size());
+      p->buckets.push_back(k);
+      if (!sbp::add_ok(shard, k.chunk, &shard) || !sbp::add_ok(flat, k.padded, &flat)) {
+        delete p;
+        return fail(SBP_ERANGE, "sbp_bucket_plan_per_tensor: total size overflows");
+      }
+    }
+    p->shard_numel = shard;
+    p->flat_numel = flat;
+    sbp::finish_flat_positions(p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(SBP_ENOMEM, "sbp_bucket_plan_per_tensor: out of host memory");
+  }
+  *out = p;
+  return ok();
+}
+
 void sbp_plan_free(sbp_plan* plan) { delete plan; }
 
 int32_t sbp_plan_num_tensors(const sbp_plan* plan) {

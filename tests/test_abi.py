@@ -255,3 +255,27 @@ def test_layout_calls_validate_before_launch():
     assert L.sbp_gather_shards(plan.handle, -1, two, V(0x100000), None) == sbp.SBP_EINVAL
     assert L.sbp_gather_shards(plan.handle, -1, (V * 2)(0x100004, 0x200000), V(0x300000),
                                None) == sbp.SBP_EALIGN
+
+
+def test_per_tensor_plan_matches_oracle():
+    rng = random.Random(8)
+    for _ in range(300):
+        T = rng.randint(0, 8)
+        rows = [rng.choice([1, 2, 3, 7, 8, 768]) for _ in range(T)]
+        numels = [r * rng.choice([0, 1, 2, 5, 13]) for r in rows]
+        N, align = rng.choice([1, 2, 3, 8]), rng.choice([1, 2, 8])
+        order = rng.choice(["reverse", "forward"])
+        use_rows = rng.random() < 0.8
+        p = sbp.bucket_plan_per_tensor(numels, N, rows if use_rows else None, align, order)
+        o = OP.per_tensor_plan(numels, N, rows if use_rows else None, align, order)
+        assert p.num_buckets == len(o.buckets) and p.flat_numel == o.flat_numel
+        for b, ob in enumerate(o.buckets):
+            assert p.bucket(b) == dict(used=ob.used, padded=ob.padded, chunk=ob.chunk,
+                                       shard_offset=ob.shard_offset, flat_offset=ob.flat_offset)
+            assert p.bucket_tensors(b) == ob.tensors
+        for t in range(T):
+            assert p.tensor(t) == (o.tensor_bucket[t], o.tensor_offset[t])
+    with pytest.raises(sbp.SbpError):
+        sbp.bucket_plan_per_tensor([31], 4, [3])
+    with pytest.raises(sbp.SbpError):
+        sbp.bucket_plan_per_tensor([30], 0, [3])

@@ -336,14 +336,19 @@ def test_clipped_step_two_shards(max_norm):
 
 # ---- layout moves: pack / unpack / shard_of / gather on both plan kinds ---------
 
-@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("kind", ["whole", "split", "per_tensor"])
 @pytest.mark.parametrize("misalign", [False, True])
-def test_layout_moves(split, misalign):
+def test_layout_moves(kind, misalign):
     import torch
     numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
     N = 4
-    pl = sbp.bucket_plan(numels, 600, N, split=split)
-    opl = OP.bucket_plan(numels, 600, N, split=split)
+    if kind == "per_tensor":
+        rows = [37, 8, 1, 13, 1, 16, 9, 25, 3, 400, 1]
+        pl = sbp.bucket_plan_per_tensor(numels, N, rows)
+        opl = OP.per_tensor_plan(numels, N, rows)
+    else:
+        pl = sbp.bucket_plan(numels, 600, N, split=kind == "split")
+        opl = OP.bucket_plan(numels, 600, N, split=kind == "split")
     grads_h = [synth.normal_bf16(31, synth.tensor_stream(1, 0, 0, t), n, 1e-2)
                for t, n in enumerate(numels)]
     keep = []

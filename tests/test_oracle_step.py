@@ -526,3 +526,72 @@ def test_clip_matches_torch_clip_grad_norm():
         if max_norm == 50.0:  # no clipping: identical to the unclipped gradient
             assert np.array_equal(ours, g)
 
+
+
+# ---- parameter groups --------------------------------------------------------------
+
+def test_grouped_step_reduces_to_plain_and_zero_decay_group():
+    n, R = 5000, 3
+    hp = synth.AdamW()
+    peers = [synth.normal_bf16(12, synth.peer_stream(1, 0, r), n, 1e-2) for r in range(R)]
+    theta = synth.normal_f32(12, synth.master_stream(0), n, 0.02)
+    z = np.zeros(n, np.float32)
+    eg = (np.arange(n) // 700 % 2).astype(np.int32)
+    same = [(hp.lr, hp.weight_decay)] * 2
+    a = S.shard_step_grouped(peers, None, S.mean_scale(R), theta, z, z, hp, same, eg, 1)
+    b = S.shard_step(peers, None, S.mean_scale(R), theta, z, z, hp, 1)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.asarray(x).view(np.uint32 if x.dtype == np.float32 else np.uint16),
+                              np.asarray(y).view(np.uint32 if y.dtype == np.float32 else np.uint16))
+    # group 1 without decay: theta' = theta - step*(m'/d) exactly (decay is 1)
+    two = [(hp.lr, hp.weight_decay), (hp.lr, 0.0)]
+    th, m1, v1, _ = S.shard_step_grouped(peers, None, S.mean_scale(R), theta, z, z, hp, two, eg, 1)
+    sc = S.adamw_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, 0.0, 1)
+    assert sc.decay == 1
+    g = S.normalise(S.reduce_peers(peers), S.mean_scale(R))
+    want = theta - sc.step_size * (m1 / (np.sqrt(v1) * sc.c2 + sc.eps))
+    sel = eg == 1
+    assert np.array_equal(th[sel], want[sel]) and not np.array_equal(th[~sel], want[~sel])
+    assert np.array_equal(m1, sc.omb1 * g)
+
+
+def test_grouped_matches_torch_param_groups():
+    """torch.optim.AdamW with two parameter groups (decay / no decay), one step
+    from the same state, within the per-step bound of the plain comparison."""
+    hp = synth.AdamW()
+    lr, b1, b2, eps, wd = (float(np.float32(x)) for x in
+                           (hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay))
+    n1, n2 = 3000, 500
+    th0 = synth.normal_f32(13, synth.master_stream(0), n1 + n2, 0.02)
+    g = S.bf16_to_f32(synth.normal_bf16(13, synth.peer_stream(1, 0, 0), n1 + n2, 1e-2))
+    p1 = torch.nn.Parameter(torch.from_numpy(th0[:n1].copy()))
+    p2 = torch.nn.Parameter(torch.from_numpy(th0[n1:].copy()))
+    opt = torch.optim.AdamW([{"params": [p1], "weight_decay": wd},
+                             {"params": [p2], "weight_decay": 0.0, "lr": lr * 2}],
+                            lr=lr, betas=(b1, b2), eps=eps, foreach=False, fused=False)
+    p1.grad = torch.from_numpy(g[:n1].copy())
+    p2.grad = torch.from_numpy(g[n1:].copy())
+    opt.step()
+    eg = np.r_[np.zeros(n1, np.int32), np.ones(n2, np.int32)]
+    z = np.zeros(n1 + n2, np.float32)
+    th, _, _, _ = S.shard_step_grouped([S.f32_to_bf16(g)], None, np.float32(1.0), th0, z, z, hp,
+                                       [(lr, wd), (lr * 2, 0.0)], eg, 1)
+    ref = np.r_[p1.detach().numpy(), p2.detach().numpy()]
+    upd = np.abs(th0 - ref) + np.abs(th0)
+    assert np.max(np.abs(th - ref) / ulp32(upd)) <= 8
+
+
+def test_shard_groups_follow_tensors_and_padding():
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3]
+    pl = P.bucket_plan(numels, 600, 4)
+    tg = [t % 3 for t in range(len(numels))]
+    for s in range(4):
+        g = S.shard_groups(pl, s, tg)
+        flat_ids = S.chunk(pl, np.arange(pl.flat_numel), s)
+        prev = 0
+        for j, fpos in enumerate(flat_ids):
+            owner = [t for t in range(len(numels)) if numels[t] and
+                     pl.tensor_flat_offset(t) <= fpos < pl.tensor_flat_offset(t) + numels[t]]
+            want = tg[owner[0]] if owner else prev
+            assert g[j] == want
+            prev = want
