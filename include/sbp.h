@@ -63,6 +63,7 @@ typedef int32_t sbp_status;
 #define SBP_ENOMEM (-5) /* host allocation failed                            */
 
 #define SBP_MAX_PEERS 16 /* largest R accepted by the reduce-type calls */
+#define SBP_MAX_GROUPS 8 /* parameter groups of the grouped AdamW step    */
 
 /* Message for the last failed call on this thread ("" if none). */
 const char* sbp_last_error(void);
@@ -315,6 +316,55 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R,
                            const float* acc, float scale, float* master,
                            float* m, float* v, void* param_out, int64_t n,
                            const sbp_adamw_hparams* hp, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Parameter groups: per-group learning rate and weight decay on one shard
+ * ("Parallelisms", ZeRO-1 and ZeRO-3: a rank updates the owned shard with
+ * the optimizer's usual per-parameter update; an optimizer's parameter
+ * groups -- decay on weight matrices, none on norms and biases -- are part
+ * of that update.  beta1, beta2, eps and the step stay shared.)
+ *
+ * sbp_group_runs (host): the run table of rank `rank`'s shard -- maximal
+ *   runs of shard elements with one group.  tensor_group: host int32[n_tensors],
+ *   each in 0..SBP_MAX_GROUPS-1.  An element of a tensor takes that tensor's
+ *   group; a padding element takes the group of the element before it in
+ *   the shard, or group 0 at the shard's start (padding is +0 with +0 state,
+ *   so it stays +0 under any group).  Runs are written as run_start[k]
+ *   (ascending, run_start[0] == 0) and run_group[k]; at most `cap` entries
+ *   are written and *count receives the number of runs (call with cap == 0
+ *   to size the arrays).  A shard of 0 elements has one run (0, 0).
+ *   Errors: SBP_EINVAL (null, rank out of range, group id out of range),
+ *   SBP_ENOMEM.
+ *
+ * sbp_adamw_shard_grouped: sbp_adamw_shard where element i takes step_size
+ *   and decay from group k's lr and weight_decay (groups[k], same rounding
+ *   rules), k = run_group[j] of the last run j with run_start[j] <= i; hp
+ *   supplies beta1, beta2, eps and step (its lr and weight_decay are not
+ *   used).  A group id outside 0..n_groups-1 in the table uses group 0.
+ *   Other arguments, layout and errors as in sbp_adamw_shard, plus:
+ *   groups      host array of n_groups (1..SBP_MAX_GROUPS) entries
+ *   run_start   device int64[n_runs], 8-B aligned, ascending, starting at 0
+ *   run_group   device int32[n_runs], 4-B aligned
+ *   n_runs      >= 1 (the table from sbp_group_runs, copied to the device)
+ *   The tables are only read; the extra traffic is a few bytes per 2048
+ *   elements (one search of the table per tile).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float lr, weight_decay;
+} sbp_group_hparams;
+
+sbp_status sbp_group_runs(const sbp_plan* plan, int32_t rank,
+                          const int32_t* tensor_group, int64_t* run_start,
+                          int32_t* run_group, int64_t cap, int64_t* count);
+sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
+                                   const float* acc, float scale,
+                                   float* master, float* m, float* v,
+                                   void* param_out, int64_t n,
+                                   const sbp_adamw_hparams* hp,
+                                   const sbp_group_hparams* groups,
+                                   int32_t n_groups, const int64_t* run_start,
+                                   const int32_t* run_group, int64_t n_runs,
+                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Global gradient-norm clipping ("Parallelisms", ZeRO-2: clipping needs the

@@ -32,7 +32,10 @@ EXPORTS = (
     "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
     "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards", "sbp_bucket_plan_per_tensor",
+    "sbp_group_runs", "sbp_adamw_shard_grouped",
 )
+
+MAX_GROUPS = 8
 
 
 class SbpError(RuntimeError):
@@ -45,6 +48,10 @@ class AdamWHParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("step", ctypes.c_int64)]
+
+
+class GroupHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float)]
 
 
 _lib = None
@@ -105,6 +112,15 @@ def lib():
                           ctypes.c_void_p, ctypes.c_void_p], st),
         "sbp_gather_shards": ([ctypes.c_void_p, ctypes.c_int32, _vpp, ctypes.c_void_p,
                                ctypes.c_void_p], st),
+        "sbp_group_runs": ([ctypes.c_void_p, ctypes.c_int32, _i32p, _i64p, _i32p,
+                            ctypes.c_int64, _i64p], st),
+        "sbp_adamw_shard_grouped": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.POINTER(AdamWHParams),
+                                     ctypes.POINTER(GroupHParams), ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -327,6 +343,66 @@ def adamw_shard(peers, acc, scale, master, m, v, param_out, hp, step, stream=Non
         None if acc is None else _f32(acc, "adamw_shard acc"), float(scale),
         _f32(master, "adamw_shard master"), _f32(m, "adamw_shard m"), _f32(v, "adamw_shard v"),
         _dev(param_out, 2, "adamw_shard param_out"), n, ctypes.byref(h),
+        _stream(stream, master)))
+
+
+def group_runs(plan, rank, tensor_group):
+    """sbp_group_runs: rank's shard as runs of one parameter group.
+
+    tensor_group: a group id (0..7) per plan tensor.  Returns numpy arrays
+    (run_start int64, run_group int32); run_start[0] == 0.
+    """
+    import numpy as np
+    g = np.ascontiguousarray(tensor_group, dtype=np.int32)
+    if g.shape != (plan.num_tensors,):
+        raise ValueError("group_runs: one group id per plan tensor")
+    gp = g.ctypes.data_as(_i32p)
+    count = ctypes.c_int64()
+    _check(lib().sbp_group_runs(plan.handle, int(rank), gp, None, None, 0, ctypes.byref(count)))
+    starts = np.zeros(count.value, dtype=np.int64)
+    groups = np.zeros(count.value, dtype=np.int32)
+    _check(lib().sbp_group_runs(plan.handle, int(rank), gp, starts.ctypes.data_as(_i64p),
+                                groups.ctypes.data_as(_i32p), count.value, ctypes.byref(count)))
+    return starts, groups
+
+
+def group_table(plan, rank, tensor_group, device):
+    """group_runs() copied to `device`: (run_start, run_group) device tensors."""
+    import torch
+    starts, groups = group_runs(plan, rank, tensor_group)
+    return (torch.from_numpy(starts).to(device), torch.from_numpy(groups).to(device))
+
+
+def adamw_shard_grouped(peers, acc, scale, master, m, v, param_out, hp, step, groups,
+                        run_start, run_group, stream=None):
+    """sbp_adamw_shard_grouped: adamw_shard() with per-group lr and weight decay.
+
+    groups: list of (lr, weight_decay), at most MAX_GROUPS; run_start/run_group:
+    the rank's run table as device tensors (int64, int32; see group_table).
+    hp supplies beta1, beta2 and eps.
+    """
+    import torch
+    n = master.numel()
+    for t, what in ((m, "m"), (v, "v"), (param_out, "param_out")):
+        if t.numel() != n:
+            raise ValueError(f"adamw_shard_grouped: {what} has the wrong size")
+    if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
+        raise ValueError("adamw_shard_grouped: peers/acc differ in size")
+    if run_start.dtype != torch.int64 or run_group.dtype != torch.int32:
+        raise ValueError("adamw_shard_grouped: run_start must be int64, run_group int32")
+    if run_start.numel() != run_group.numel():
+        raise ValueError("adamw_shard_grouped: run tables differ in length")
+    if not 1 <= len(groups) <= MAX_GROUPS:
+        raise ValueError(f"adamw_shard_grouped: 1..{MAX_GROUPS} groups")
+    h = AdamWHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, int(step))
+    gs = (GroupHParams * len(groups))(*[GroupHParams(lr, wd) for lr, wd in groups])
+    _check(lib().sbp_adamw_shard_grouped(
+        _ptrs(peers, "adamw_shard_grouped peers"), len(peers),
+        None if acc is None else _f32(acc, "adamw_shard_grouped acc"), float(scale),
+        _f32(master, "adamw_shard_grouped master"), _f32(m, "adamw_shard_grouped m"),
+        _f32(v, "adamw_shard_grouped v"), _dev(param_out, 2, "adamw_shard_grouped param_out"), n,
+        ctypes.byref(h), gs, len(groups), _dev(run_start, 8, "adamw_shard_grouped run_start"),
+        _dev(run_group, 4, "adamw_shard_grouped run_group"), run_start.numel(),
         _stream(stream, master)))
 
 

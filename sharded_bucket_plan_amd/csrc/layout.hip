@@ -315,4 +315,46 @@ sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket, const void* c
   return launch_segments(who, segs, stream);
 }
 
+sbp_status sbp_group_runs(const sbp_plan* plan, int32_t rank, const int32_t* tensor_group,
+                          int64_t* run_start, int32_t* run_group, int64_t cap, int64_t* count) {
+  if (plan == nullptr || tensor_group == nullptr || count == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_group_runs: null argument");
+  if (cap > 0 && (run_start == nullptr || run_group == nullptr))
+    return sbp::fail(SBP_EINVAL, "sbp_group_runs: null output arrays");
+  if (rank < 0 || rank >= plan->world_n)
+    return sbp::fail(SBP_EINVAL, "sbp_group_runs: rank out of range");
+  const int32_t T = static_cast<int32_t>(plan->numel.size());
+  for (int32_t t = 0; t < T; ++t)
+    if (tensor_group[t] < 0 || tensor_group[t] >= SBP_MAX_GROUPS)
+      return sbp::fail(SBP_EINVAL, "sbp_group_runs: group ids must be in 0..7");
+  // Leading padding is group 0; later padding extends the run before it;
+  // neighbouring pieces of the same group merge.
+  std::vector<std::pair<int64_t, int32_t>> runs;
+  try {
+    runs.push_back({0, 0});
+    for (const sbp::Bucket& b : plan->buckets) {
+      const int64_t lo = b.flat_offset + rank * b.chunk, hi = lo + b.chunk;
+      for (const Piece& pc : pieces_in(plan, lo, hi)) {
+        const int64_t at = b.shard_offset + (pc.flat - lo);
+        const int32_t g = tensor_group[pc.t];
+        if (g == runs.back().second) continue;
+        if (at == runs.back().first)
+          runs.back().second = g;  // the run before had no elements of its own
+        else
+          runs.push_back({at, g});
+        if (runs.size() >= 2 && runs[runs.size() - 2].second == runs.back().second)
+          runs.pop_back();  // merged with the one before
+      }
+    }
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_group_runs: out of host memory");
+  }
+  for (size_t i = 0; i < runs.size() && static_cast<int64_t>(i) < cap; ++i) {
+    run_start[i] = runs[i].first;
+    run_group[i] = runs[i].second;
+  }
+  *count = static_cast<int64_t>(runs.size());
+  return sbp::ok();
+}
+
 }  // extern "C"

@@ -92,6 +92,16 @@ struct Scalars {
   float b1, b2, omb1, omb2, eps, step_size, c2, decay;
 };
 
+// Parameter groups of the grouped step: the shard's run table (device) and
+// each group's step size and decay (binary32, unused slots hold group 0's).
+struct GroupArgs {
+  const int64_t* run_start;
+  const int32_t* run_group;
+  int64_t n_runs;
+  float step_size[SBP_MAX_GROUPS];
+  float decay[SBP_MAX_GROUPS];
+};
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_one(uint16_t h) {
@@ -114,6 +124,56 @@ __device__ __forceinline__ void adamw_one(float g, float& th, float& m, float& v
   th = th * s.decay - s.step_size * (m1 / d);
   m = m1;
   v = v1;
+}
+
+// Last run whose start is <= x (run 0 if none is).  Uniform when x is.
+__device__ __forceinline__ int64_t find_run(const int64_t* __restrict__ rs, int64_t nr,
+                                            int64_t x) {
+  int64_t a = 0, b = nr;
+  while (b - a > 1) {
+    const int64_t mid = a + ((b - a) >> 1);
+    if (rs[mid] <= x) a = mid;
+    else b = mid;
+  }
+  return a;
+}
+
+// Step size and decay of group g (a chain of selects: the table stays in
+// kernel arguments, no indexed private copy); ids outside 1..7 take group 0.
+__device__ __forceinline__ void group_pick(const GroupArgs& ga, int32_t g, float& step_size,
+                                           float& decay) {
+  step_size = ga.step_size[0];
+  decay = ga.decay[0];
+#pragma unroll
+  for (int k = 1; k < SBP_MAX_GROUPS; ++k) {
+    step_size = g == k ? ga.step_size[k] : step_size;
+    decay = g == k ? ga.decay[k] : decay;
+  }
+}
+
+// Per-element step size and decay of the lane's 8 elements [e0, e0+8) in a
+// tile [lo, lo + 2048).  One search per block (block-uniform, in scalar
+// loads); only a tile that holds a run boundary looks elements up one by one.
+__device__ __forceinline__ void group_scalars8(const GroupArgs& ga, int64_t lo, int64_t e0,
+                                               float (&ss)[8], float (&dc)[8]) {
+  const int64_t nr = ga.n_runs;
+  const int64_t k = find_run(ga.run_start, nr, lo);
+  if (k + 1 >= nr || ga.run_start[k + 1] >= lo + static_cast<int64_t>(kBlock) * 8) {
+    float a, b;
+    group_pick(ga, ga.run_group[k], a, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ss[j] = a;
+      dc[j] = b;
+    }
+  } else {
+    int64_t kk = k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      while (kk + 1 < nr && ga.run_start[kk + 1] <= e0 + j) ++kk;
+      group_pick(ga, ga.run_group[kk], ss[j], dc[j]);
+    }
+  }
 }
 
 // Group (8 elements) handled by this lane, tiles in XCD-contiguous order.
@@ -225,12 +285,13 @@ accumulate_kernel(Peers P, float* __restrict__ acc, int64_t n) {
 }
 
 // ---- fused: G = [acc +] S, g = G*scale, AdamW, bf16 emit --------------------
-template <int R, bool ACC>
+// GROUPED: step size and decay per element from the run table in `ga`.
+template <int R, bool ACC, bool GROUPED>
 __global__ void __launch_bounds__(kBlock)
 fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
                    float* __restrict__ master, float* __restrict__ mom1,
                    float* __restrict__ mom2, uint16_t* __restrict__ pout, int64_t n,
-                   Scalars s) {
+                   Scalars s, GroupArgs ga) {
   static_assert(R > 0 || ACC, "R == 0 needs the accumulator");
   const int64_t groups = n >> 3;
   const int64_t gi = my_group();
@@ -254,10 +315,23 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
       for (int j = 0; j < 8; ++j) G[j] = A[j];
     }
     uint32_t pb[8];
+    if constexpr (GROUPED) {
+      float ss[8], dc[8];
+      group_scalars8(ga, (gi - threadIdx.x) * 8, gi * 8, ss, dc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      adamw_one(G[j] * scale, th[j], m[j], v[j], s);
-      pb[j] = bf16_rne(th[j]);
+      for (int j = 0; j < 8; ++j) {
+        Scalars sj = s;
+        sj.step_size = ss[j];
+        sj.decay = dc[j];
+        adamw_one(G[j] * scale, th[j], m[j], v[j], sj);
+        pb[j] = bf16_rne(th[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        adamw_one(G[j] * scale, th[j], m[j], v[j], s);
+        pb[j] = bf16_rne(th[j]);
+      }
     }
     store8(master, gi, th);
     store8(mom1, gi, m);
@@ -277,7 +351,11 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
         G = acc[i];
       }
       float th = master[i], m = mom1[i], v = mom2[i];
-      adamw_one(G * scale, th, m, v, s);
+      Scalars si = s;
+      if constexpr (GROUPED)
+        group_pick(ga, ga.run_group[find_run(ga.run_start, ga.n_runs, i)], si.step_size,
+                   si.decay);
+      adamw_one(G * scale, th, m, v, si);
       master[i] = th;
       mom1[i] = m;
       mom2[i] = v;
@@ -502,17 +580,25 @@ sbp_status dispatch_r(int32_t R, F&& f) {
   }
 }
 
-// Host scalars of one AdamW step: float64 from the binary32 hyperparameters,
-// each rounded once to binary32; beta^t by t multiplications.
-Scalars adamw_scalars(const sbp_adamw_hparams& hp) {
-  const double lr = hp.lr, b1 = hp.beta1, b2 = hp.beta2, wd = hp.weight_decay;
+// Bias corrections 1 - b1^t and 1 - b2^t in float64 from the binary32 betas;
+// beta^t by t multiplications.
+void bias_corrections(const sbp_adamw_hparams& hp, double& bc1, double& bc2) {
+  const double b1 = hp.beta1, b2 = hp.beta2;
   double b1t = 1.0, b2t = 1.0;
   for (int64_t k = 0; k < hp.step; ++k) {
     b1t *= b1;
     b2t *= b2;
     if (b1t == 0.0 && b2t == 0.0) break;  // both powers have underflowed for good
   }
-  const double bc1 = 1.0 - b1t, bc2 = 1.0 - b2t;
+  bc1 = 1.0 - b1t;
+  bc2 = 1.0 - b2t;
+}
+
+// Host scalars of one AdamW step: float64 from the binary32 hyperparameters,
+// each rounded once to binary32.  step_size and decay use (lr, wd).
+Scalars adamw_scalars(const sbp_adamw_hparams& hp, double bc1, double bc2, float lr_f,
+                      float wd_f) {
+  const double lr = lr_f, wd = wd_f, b1 = hp.beta1, b2 = hp.beta2;
   Scalars s;
   s.b1 = hp.beta1;
   s.b2 = hp.beta2;
@@ -598,28 +684,31 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers, int32_t R,
   });
 }
 
-sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc, float scale,
-                           float* master, float* m, float* v, void* param_out, int64_t n,
-                           const sbp_adamw_hparams* hp, hipStream_t stream) {
-  const char* who = "sbp_adamw_shard";
-  if (R < 0 || R > SBP_MAX_PEERS)
-    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: R must be in 0..16");
-  if (n < 0) return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: n < 0");
-  if (hp == nullptr) return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: hp is null");
-  if (hp->step < 1) return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: step must be >= 1");
-  if (n == 0) return sbp::ok();  // nothing is read or written
-  Peers P;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the fused entry points; fills P.
+sbp_status check_fused(const char* who, const void* const* peers, int32_t R, const float* acc,
+                       float* master, float* m, float* v, void* param_out, int64_t n,
+                       const sbp_adamw_hparams* hp, Peers& P) {
+  const std::string w(who);
+  if (R < 0 || R > SBP_MAX_PEERS) return sbp::fail(SBP_EINVAL, w + ": R must be in 0..16");
+  if (n < 0) return sbp::fail(SBP_EINVAL, w + ": n < 0");
+  if (hp == nullptr) return sbp::fail(SBP_EINVAL, w + ": hp is null");
+  if (hp->step < 1) return sbp::fail(SBP_EINVAL, w + ": step must be >= 1");
+  if (n == 0) return SBP_OK;
   sbp_status st = collect_peers(who, peers, R, P);
   if (st != SBP_OK) return st;
   if (R == 0 && acc == nullptr)
-    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: R == 0 needs an accumulator");
+    return sbp::fail(SBP_EINVAL, w + ": R == 0 needs an accumulator");
   if (master == nullptr || m == nullptr || v == nullptr || param_out == nullptr)
-    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: null state or output pointer");
+    return sbp::fail(SBP_EINVAL, w + ": null state or output pointer");
   const void* dev[5] = {acc, master, m, v, param_out};
   for (const void* p : dev)
     if (p != nullptr && !sbp::aligned(p, 16))
-      return sbp::fail(SBP_EALIGN, "sbp_adamw_shard: device pointers must be 16-byte aligned");
-  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_adamw_shard: n too large");
+      return sbp::fail(SBP_EALIGN, w + ": device pointers must be 16-byte aligned");
+  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, w + ": n too large");
   // pairwise disjoint: acc, master, m, v, param_out and the peers
   const void* ptr[5 + SBP_MAX_PEERS];
   int64_t len[5 + SBP_MAX_PEERS];
@@ -633,24 +722,96 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc
   for (int a = 0; a < 5; ++a)  // outputs (and acc) against everything else
     for (int b = a + 1; b < k; ++b)
       if (sbp::overlaps(ptr[a], len[a], ptr[b], len[b]))
-        return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: buffers overlap");
-  const Scalars s = adamw_scalars(*hp);
+        return sbp::fail(SBP_EINVAL, w + ": buffers overlap");
+  return SBP_OK;
+}
+
+// Launches the fused kernel for the runtime R and accumulator presence.
+template <bool GROUPED>
+sbp_status launch_fused(const char* who, const Peers& P, int32_t R, const float* acc, float scale,
+                        float* master, float* m, float* v, void* param_out, int64_t n,
+                        const Scalars& s, const GroupArgs& ga, hipStream_t stream) {
   uint16_t* pout = static_cast<uint16_t*>(param_out);
   const int lane_bytes = 16 * R + 96 + (acc ? 32 : 0);
   (void)hipGetLastError();
   return dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
     if constexpr (RR == 0) {
-      return launch(who, fused_adamw_kernel<0, true>, n, lane_bytes, stream, P, acc, scale,
-                    master, m, v, pout, n, s);
+      return launch(who, fused_adamw_kernel<0, true, GROUPED>, n, lane_bytes, stream, P, acc,
+                    scale, master, m, v, pout, n, s, ga);
     } else if (acc) {
-      return launch(who, fused_adamw_kernel<RR, true>, n, lane_bytes, stream, P, acc, scale,
-                    master, m, v, pout, n, s);
+      return launch(who, fused_adamw_kernel<RR, true, GROUPED>, n, lane_bytes, stream, P, acc,
+                    scale, master, m, v, pout, n, s, ga);
     } else {
-      return launch(who, fused_adamw_kernel<RR, false>, n, lane_bytes, stream, P, acc, scale,
-                    master, m, v, pout, n, s);
+      return launch(who, fused_adamw_kernel<RR, false, GROUPED>, n, lane_bytes, stream, P, acc,
+                    scale, master, m, v, pout, n, s, ga);
     }
   });
+}
+
+}  // namespace
+
+extern "C" {
+
+sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc, float scale,
+                           float* master, float* m, float* v, void* param_out, int64_t n,
+                           const sbp_adamw_hparams* hp, hipStream_t stream) {
+  const char* who = "sbp_adamw_shard";
+  Peers P;
+  sbp_status st = check_fused(who, peers, R, acc, master, m, v, param_out, n, hp, P);
+  if (st != SBP_OK) return st;
+  if (n == 0) return sbp::ok();  // nothing is read or written
+  const GroupArgs none{};
+  double bc1, bc2;
+  bias_corrections(*hp, bc1, bc2);
+  return launch_fused<false>(who, P, R, acc, scale, master, m, v, param_out, n,
+                             adamw_scalars(*hp, bc1, bc2, hp->lr, hp->weight_decay), none,
+                             stream);
+}
+
+sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R, const float* acc,
+                                   float scale, float* master, float* m, float* v,
+                                   void* param_out, int64_t n, const sbp_adamw_hparams* hp,
+                                   const sbp_group_hparams* groups, int32_t n_groups,
+                                   const int64_t* run_start, const int32_t* run_group,
+                                   int64_t n_runs, hipStream_t stream) {
+  const char* who = "sbp_adamw_shard_grouped";
+  Peers P;
+  sbp_status st = check_fused(who, peers, R, acc, master, m, v, param_out, n, hp, P);
+  if (st != SBP_OK) return st;
+  if (groups == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: groups is null");
+  if (n_groups < 1 || n_groups > SBP_MAX_GROUPS)
+    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: n_groups must be in 1..8");
+  if (n_runs < 1) return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: n_runs must be >= 1");
+  if (n == 0) return sbp::ok();  // nothing is read or written
+  if (run_start == nullptr || run_group == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: run table is null");
+  if (!sbp::aligned(run_start, 8) || !sbp::aligned(run_group, 4))
+    return sbp::fail(SBP_EALIGN, "sbp_adamw_shard_grouped: run table misaligned");
+  if (n_runs > INT64_MAX / 8)
+    return sbp::fail(SBP_ERANGE, "sbp_adamw_shard_grouped: n_runs too large");
+  // the run table is read while the outputs are written
+  const void* outs[4] = {master, m, v, param_out};
+  const int64_t out_len[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+  for (int a = 0; a < 4; ++a)
+    if (sbp::overlaps(outs[a], out_len[a], run_start, 8 * n_runs) ||
+        sbp::overlaps(outs[a], out_len[a], run_group, 4 * n_runs))
+      return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: run table overlaps an output");
+  double bc1, bc2;
+  bias_corrections(*hp, bc1, bc2);
+  const Scalars s = adamw_scalars(*hp, bc1, bc2, groups[0].lr, groups[0].weight_decay);
+  GroupArgs ga{};
+  ga.run_start = run_start;
+  ga.run_group = run_group;
+  ga.n_runs = n_runs;
+  for (int k = 0; k < SBP_MAX_GROUPS; ++k) {
+    const sbp_group_hparams& g = groups[k < n_groups ? k : 0];
+    const Scalars sk = adamw_scalars(*hp, bc1, bc2, g.lr, g.weight_decay);
+    ga.step_size[k] = sk.step_size;
+    ga.decay[k] = sk.decay;
+  }
+  return launch_fused<true>(who, P, R, acc, scale, master, m, v, param_out, n, s, ga, stream);
 }
 
 // Workspace of the squared norm: the tile partials, then each tree level.

@@ -279,3 +279,113 @@ def test_per_tensor_plan_matches_oracle():
         sbp.bucket_plan_per_tensor([31], 4, [3])
     with pytest.raises(sbp.SbpError):
         sbp.bucket_plan_per_tensor([30], 0, [3])
+
+
+def _expand_runs(starts, groups, n):
+    import numpy as np
+    out = np.empty(n, dtype=np.int32)
+    ends = list(starts[1:]) + [n]
+    for a, e, g in zip(starts, ends, groups):
+        out[a:e] = g
+    return out
+
+
+def _check_runs(p, o, T, rng):
+    """group_runs() of every rank equals the run-length encoding of the
+    oracle's per-element groups (starts ascending from 0, neighbours differ)."""
+    import numpy as np
+    from oracle import step as OS
+    tg = [rng.randrange(sbp.MAX_GROUPS) if rng.random() < 0.7 else rng.randrange(2)
+          for _ in range(T)]
+    for s in range(p.world_n):
+        starts, groups = sbp.group_runs(p, s, tg)
+        assert starts[0] == 0 and len(starts) == len(groups) >= 1
+        assert np.all(np.diff(starts) > 0) and np.all(groups[1:] != groups[:-1])
+        assert (p.shard_numel == 0) == (starts[-1] >= p.shard_numel)
+        want = OS.shard_groups(o, s, tg)
+        assert np.array_equal(_expand_runs(starts, groups, p.shard_numel), want)
+
+
+def test_group_runs_match_oracle():
+    rng = random.Random(11)
+    for _ in range(150):
+        T = rng.randint(0, 9)
+        numels = [rng.choice([0, 1, 3, 8, 13, 40, 257]) for _ in range(T)]
+        N = rng.choice([1, 2, 3, 8])
+        cap = rng.choice([16, 64, 200, 1 << 20])
+        kind = rng.choice(["whole", "split", "per_tensor"])
+        if kind == "per_tensor":
+            align = rng.choice([1, 2, 8])
+            p = sbp.bucket_plan_per_tensor(numels, N, None, align)
+            o = OP.per_tensor_plan(numels, N, None, align)
+        else:
+            split = kind == "split"
+            p = sbp.bucket_plan(numels, cap, N, split=split)
+            o = OP.bucket_plan(numels, cap, N, split=split)
+        _check_runs(p, o, T, rng)
+
+
+def test_group_runs_on_workloads():
+    rng = random.Random(12)
+    for name in ("tiny_mlp", "gpt2_small"):
+        w = synth.WORKLOADS[name]
+        p = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+        o = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+        _check_runs(p, o, len(w.numels), rng)
+
+
+def test_group_runs_validate():
+    L = sbp.lib()
+    plan = sbp.bucket_plan([10, 20], 1 << 20, 2)
+    G = ctypes.c_int32 * 2
+    cnt = ctypes.c_int64()
+    assert L.sbp_group_runs(plan.handle, 0, G(0, 8), None, None, 0, ctypes.byref(cnt)) \
+        == sbp.SBP_EINVAL
+    assert L.sbp_group_runs(plan.handle, 0, G(-1, 0), None, None, 0, ctypes.byref(cnt)) \
+        == sbp.SBP_EINVAL
+    assert L.sbp_group_runs(plan.handle, 2, G(0, 1), None, None, 0, ctypes.byref(cnt)) \
+        == sbp.SBP_EINVAL
+    assert L.sbp_group_runs(None, 0, G(0, 1), None, None, 0, ctypes.byref(cnt)) == sbp.SBP_EINVAL
+    assert L.sbp_group_runs(plan.handle, 0, G(0, 1), None, None, 1, ctypes.byref(cnt)) \
+        == sbp.SBP_EINVAL
+    assert L.sbp_group_runs(plan.handle, 0, G(0, 1), None, None, 0, ctypes.byref(cnt)) \
+        == sbp.SBP_OK and cnt.value >= 1
+    # a short output array gets the first `cap` runs and the full count
+    starts = (ctypes.c_int64 * 1)()
+    groups = (ctypes.c_int32 * 1)()
+    assert L.sbp_group_runs(plan.handle, 0, G(3, 5), starts, groups, 1, ctypes.byref(cnt)) \
+        == sbp.SBP_OK
+    full_s, full_g = sbp.group_runs(plan, 0, [3, 5])
+    assert cnt.value == len(full_s) and starts[0] == full_s[0] and groups[0] == full_g[0]
+
+
+def test_grouped_step_validates_before_launch():
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    peers = (V * 2)(0x100000, 0x200000)
+    hp = sbp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    gs = (sbp.GroupHParams * 2)(sbp.GroupHParams(1e-3, 0.1), sbp.GroupHParams(1e-3, 0.0))
+    ok = dict(peers=peers, R=2, acc=None, scale=0.5, master=V(0x300000), m=V(0x400000),
+              v=V(0x500000), p=V(0x600000), n=1024, hp=ctypes.byref(hp), groups=gs, ng=2,
+              rs=V(0x700000), rg=V(0x800000), nr=3)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.sbp_adamw_shard_grouped(a["peers"], a["R"], a["acc"], a["scale"], a["master"],
+                                         a["m"], a["v"], a["p"], a["n"], a["hp"], a["groups"],
+                                         a["ng"], a["rs"], a["rg"], a["nr"], None)
+
+    assert call(R=17) == sbp.SBP_EINVAL
+    assert call(groups=None) == sbp.SBP_EINVAL
+    assert call(ng=0) == sbp.SBP_EINVAL
+    assert call(ng=9) == sbp.SBP_EINVAL
+    assert call(nr=0) == sbp.SBP_EINVAL
+    assert call(rs=None) == sbp.SBP_EINVAL
+    assert call(rs=V(0x700004)) == sbp.SBP_EALIGN
+    assert call(rg=V(0x800002)) == sbp.SBP_EALIGN
+    assert call(rs=V(0x300000 + 64)) == sbp.SBP_EINVAL  # inside master
+    assert call(rg=V(0x600000 + 64)) == sbp.SBP_EINVAL  # inside param_out
+    assert call(master=V(0x300004)) == sbp.SBP_EALIGN
+    assert call(m=V(0x300000 + 1024)) == sbp.SBP_EINVAL
+    assert call(n=0) == sbp.SBP_OK
+    assert call(n=0, rs=None, rg=None) == sbp.SBP_OK

@@ -137,6 +137,90 @@ def test_adamw_shard_acc_only():
     assert H.assert_state_close(got, want, "acc only") == 0
 
 
+GROUPS = [(1e-3, 0.1), (5e-4, 0.0), (2e-3, 0.01)]
+
+
+def _random_runs(n, rng):
+    """A run table over n elements: runs of 1 element to several tiles, starts
+    off the 8-element grid, and ids outside 0..len(GROUPS)-1 (which take
+    group 0)."""
+    starts, pos = [0], 0
+    while True:
+        pos += int(rng.choice([1, 3, 8, 17, 100, 2048, 5000, 40000]))
+        if pos >= n:
+            break
+        starts.append(pos)
+    groups = rng.integers(-1, len(GROUPS) + 6, len(starts)).astype(np.int32)
+    return np.array(starts, np.int64), groups
+
+
+def _elem_groups(starts, groups, n):
+    g = np.empty(n, np.int64)
+    ends = list(starts[1:]) + [n]
+    for a, e, k in zip(starts, ends, groups):
+        g[a:e] = k if 0 <= k < len(GROUPS) else 0
+    return g
+
+
+@pytest.mark.parametrize("R", [0, 1, 8])
+@pytest.mark.parametrize("n", SIZES + [BIG])
+def test_adamw_shard_grouped(R, n):
+    """Per-group lr and weight decay from a run table, every element."""
+    import torch
+    if n == BIG and R != 8:
+        pytest.skip("big size runs at R=8 only")
+    rng = np.random.default_rng(n * 31 + R)
+    starts, groups = _random_runs(n, rng)
+    eg = _elem_groups(starts, groups, n)
+    rs, rg = torch.from_numpy(starts).to(H.dev()), torch.from_numpy(groups).to(H.dev())
+    th, m, v = _state(16, n)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    pw, dp, g = H.guarded(n, 2)
+    acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if R == 0 else None
+    want = (th, m, v, None)
+    bufs = None
+    for t in (1, 2):
+        acc_h = None
+        if R == 0:
+            sbp.accumulate_grads(acc_d, H.dev_peers(16, t, 0, 3, n, 1e-3), first=True)
+            acc_h = OS.reduce_peers(H.host_peers(16, t, 0, 3, n, 1e-3))
+        else:
+            bufs = H.dev_peers(16, t, 1, R, n, 1e-3, bufs)
+        scale = sbp.mean_scale(max(R, 3))
+        sbp.adamw_shard_grouped(bufs or [], acc_d, scale, dth, dm, dv, dp, HP, t, GROUPS, rs, rg)
+        peers_h = H.host_peers(16, t, 1, R, n, 1e-3) if R else []
+        want = OS.shard_step_grouped(peers_h, acc_h, np.float32(scale), want[0], want[1],
+                                     want[2], HP, GROUPS, eg, t)
+    torch.cuda.synchronize()
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
+        H.assert_bits_equal(a, b, f"grouped R={R} n={n} {name}")
+    assert H.canaries_intact(pw, g)
+
+
+def test_adamw_shard_grouped_one_group_is_plain():
+    """One run of one group: the grouped step equals the plain step."""
+    import torch
+    n = 256 * 8 * 5 + 3
+    th, m, v = _state(17, n)
+    outs = []
+    for grouped in (False, True):
+        dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+        dp = H.empty_u16(n)
+        peers = H.dev_peers(17, 1, 0, 4, n, 1e-3)
+        if grouped:
+            rs = torch.zeros(1, dtype=torch.int64, device=H.dev())
+            rg = torch.zeros(1, dtype=torch.int32, device=H.dev())
+            sbp.adamw_shard_grouped(peers, None, 0.25, dth, dm, dv, dp, HP, 1,
+                                    [(HP.lr, HP.weight_decay)], rs, rg)
+        else:
+            sbp.adamw_shard(peers, None, 0.25, dth, dm, dv, dp, HP, 1)
+        torch.cuda.synchronize()
+        outs.append((H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp)))
+    for a, b, name in zip(outs[0], outs[1], ("master", "m", "v", "param")):
+        H.assert_bits_equal(b, a, f"one group {name}")
+
+
 def test_empty_inputs_touch_nothing():
     import torch
     whole, out, g = H.guarded(0, 4)

@@ -98,6 +98,43 @@ def test_gpt2_small_full():
         H.assert_bits_equal(a, b, f"gpt2_small {name}")
 
 
+def test_gpt2_small_grouped_full():
+    """GPT-2-small shard with the usual two parameter groups -- weight decay
+    on matrices, none on biases, norm gains and other 1-D tensors -- plus a
+    lower lr on the embeddings (a third group); run table from the plan,
+    two steps, every element."""
+    import torch
+    w = synth.WORKLOADS["gpt2_small"]
+    hp = _hp(w)
+    pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    opl = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    n = pl.shard_numel
+    groups = [(hp.lr, hp.weight_decay), (hp.lr, 0.0), (hp.lr * 0.5, hp.weight_decay)]
+    tg = [1 if len(shape) == 1 else (2 if "wte" in name or "wpe" in name else 0)
+          for name, shape in w.params]
+    assert set(tg) == {0, 1, 2}
+    s = 3
+    rs, rg = sbp.group_table(pl, s, tg, H.dev())
+    eg = OS.shard_groups(opl, s, tg)
+    th = synth.normal_f32(SEED, synth.master_stream(s), n, w.master_sigma)
+    z = np.zeros(n, np.float32)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(z), H.from_np_f32(z)
+    dp = H.empty_u16(n)
+    bufs = None
+    want = (th, z, z, None)
+    for t in (1, 2):
+        bufs = H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, bufs)
+        sbp.adamw_shard_grouped(bufs, None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t,
+                                groups, rs, rg)
+        want = OS.shard_step_grouped(H.host_peers(SEED, t, 0, w.R, n, w.grad_sigma), None,
+                                     OS.mean_scale(w.R), want[0], want[1], want[2], hp,
+                                     groups, eg, t)
+    torch.cuda.synchronize()
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
+        H.assert_bits_equal(a, b, f"gpt2_small grouped {name}")
+
+
 def _sample_index(plan, n, count, seed):
     """Random elements plus the first and last element of every bucket's chunk
     and the shard's last 16 elements (ragged ends of each launch range)."""
