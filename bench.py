@@ -64,7 +64,7 @@ def fused_bytes_per_elem(R, acc):
 class Workload:
     """Device buffers and the per-step launches of one workload."""
 
-    def __init__(self, name, seed, clip=None):
+    def __init__(self, name, seed, clip=None, groups=False):
         import torch
         import sharded_bucket_plan_amd as sbp
         import synth
@@ -80,6 +80,13 @@ class Workload:
         self.n = self.plan.shard_numel
         self.acc = w.K > 1
         self.clip = clip
+        self.groups = None
+        if groups:
+            # the usual two parameter groups: decay on matrices, none on 1-D
+            # tensors (biases, norm gains); run table of this rank's shard
+            tg = [1 if len(shape) == 1 else 0 for _, shape in w.params]
+            self.groups = [(self.hp.lr, self.hp.weight_decay), (self.hp.lr, 0.0)]
+            self.runs = sbp.group_table(self.plan, w.shard_index, tg, self.dev)
         # with clipping the update reads G (fp32) written by the norm pass
         self.bytes_fused = (fused_bytes_per_elem(0, True) if clip else
                             fused_bytes_per_elem(w.R, self.acc)) * self.n
@@ -181,8 +188,12 @@ class Workload:
             mark("fused_adamw_kernel", 1)
             return
         mark("fused_adamw_kernel", 0)
-        sbp.adamw_shard(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"], s["p"],
-                        self.hp, t)
+        if self.groups:
+            sbp.adamw_shard_grouped(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"],
+                                    s["p"], self.hp, t, self.groups, *self.runs)
+        else:
+            sbp.adamw_shard(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"],
+                            s["p"], self.hp, t)
         mark("fused_adamw_kernel", 1)
 
     def config(self):
@@ -192,6 +203,8 @@ class Workload:
                 "bucket_cap_MiB": w.bucket_cap_bytes >> 20, "buckets": self.plan.num_buckets,
                 "pack": w.pack, "rotating_buffer_sets": self.nsets,
                 "clip_max_norm": self.clip,
+                "param_groups": len(self.groups) if self.groups else 1,
+                "group_runs": int(self.runs[0].numel()) if self.groups else 1,
                 "fused_bytes_per_elem": self.bytes_fused // self.n}
 
 
@@ -437,6 +450,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--clip", type=float, default=None, metavar="MAX_NORM",
                     help="add global gradient-norm clipping to the step")
+    ap.add_argument("--groups", action="store_true",
+                    help="two parameter groups (no weight decay on 1-D tensors): the grouped "
+                         "fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--bucket-sweep", action="store_true",
@@ -472,7 +488,9 @@ def main():
                           "bytes_each_way": COPY_BYTES, "calls": CALIBRATION_CALLS}))
         return
     log(f"bench: workload {args.workload}, allocating and generating inputs on cuda:0")
-    W = Workload(args.workload, seed, args.clip)
+    if args.groups and args.clip:
+        raise SystemExit("bench.py: --groups and --clip are separate measurements")
+    W = Workload(args.workload, seed, args.clip, args.groups)
     log(f"bench: n={W.n} R={W.w.R} sets={W.nsets}; warmup {args.warmup}")
     t = 0
     for _ in range(args.warmup):
@@ -509,7 +527,8 @@ def main():
     log(f"bench: {ms_per_step:.4f} ms/step, fused kernel {kern_avg:.4f} ms avg "
         f"(min {min(kern_ms):.4f}), {achieved:.1f} GB/s algorithmic")
 
-    traffic = traffic_from_profile(bytes_fused)
+    # the committed counters are of the plain fused kernel
+    traffic = None if args.groups else traffic_from_profile(bytes_fused)
     copy_gbs = None
     if not args.no_copy_ceiling:
         del W
