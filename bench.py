@@ -147,7 +147,7 @@ class Workload:
         w, n = self.w, self.n
         out = []
         if w.pack:
-            out.append(("pack_kernel", 4 * sum(w.numels) + 2 * (self.plan.flat_numel - sum(w.numels))))
+            out.append(("copy_kernel", 4 * sum(w.numels) + 2 * (self.plan.flat_numel - sum(w.numels))))
         if self.acc:
             out.append(("accumulate_kernel", (2 * w.R + 4) * n + (2 * w.R + 8) * n * (w.K - 2)))
         if self.clip:
@@ -167,9 +167,9 @@ class Workload:
                 ev[part][k].record()
 
         if w.pack:
-            mark("pack_kernel", 0)
+            mark("copy_kernel", 0)
             sbp.pack_grads(self.plan, s["grads"], s["flat0"])
-            mark("pack_kernel", 1)
+            mark("copy_kernel", 1)
         if self.acc:
             mark("accumulate_kernel", 0)
             for k in range(w.K - 1):
