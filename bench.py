@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -334,6 +335,17 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, command)
     print("\n".join(lines))
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(workload_name, seed, target_s):
     """The oracle as it stands, on a bounded contiguous sample of the same
     workload's shard (inputs generated on the host), single-threaded numpy."""
@@ -361,7 +373,8 @@ def cpu_baseline(workload_name, seed, target_s):
         i0 += chunk
     b = fused_bytes_per_elem(w.R, w.K > 1)
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "gbs": done * b / spent / 1e9,
+            "gbs": done * b / spent / 1e9, "host_cpu": host_cpu_model(),
+            "host_threads_available": os.cpu_count(),
             "sample": (f"{done} elements ({done // chunk} contiguous slices of {chunk}) of the "
                        f"{workload_name} shard, one fused step (R={w.R}"
                        f"{', with accumulator' if w.K > 1 else ''}), numpy binary32 oracle, "
@@ -516,7 +529,8 @@ def main():
         ms = [e[p][0].elapsed_time(e[p][1]) for e in evs]
         avg = sum(ms) / len(ms)
         gbs = nbytes / (avg * 1e-3) / 1e9
-        kernels[p] = {"ms_avg": avg, "ms_min": min(ms), "algorithmic_bytes": nbytes,
+        kernels[p] = {"ms_avg": avg, "ms_median": statistics.median(ms), "ms_min": min(ms),
+                      "algorithmic_bytes": nbytes,
                       "gbs": gbs, "frac": gbs / PEAK_GBS}
     kern_ms = [e["fused_adamw_kernel"][0].elapsed_time(e["fused_adamw_kernel"][1]) for e in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)

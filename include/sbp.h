@@ -109,7 +109,8 @@ const char* sbp_version(void);
  *                    A plan is read-only after creation and may be shared
  *                    between threads.
  * Errors: SBP_EINVAL (null, n_tensors < 0, negative numel, bad cap/N/align/
- * flags), SBP_ERANGE (a sum overflows int64), SBP_ENOMEM.
+ * flags), SBP_ERANGE (a flat size beyond 2^62 elements (2^61 split), or a
+ * split plan of more than 2^24 buckets), SBP_ENOMEM.
  * ---------------------------------------------------------------------- */
 typedef struct sbp_plan sbp_plan;
 

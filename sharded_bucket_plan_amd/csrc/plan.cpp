@@ -35,6 +35,10 @@ sbp_status ok() {
 
 namespace {
 
+// A plan with more buckets than this is a caller error (a cap far below the
+// model size); refusing it keeps the host tables bounded.
+constexpr int64_t kMaxBuckets = int64_t{1} << 24;
+
 bool add_ok(int64_t a, int64_t b, int64_t* out) {
   return !__builtin_add_overflow(a, b, out);
 }
@@ -87,8 +91,9 @@ sbp_status split_plan(sbp_plan* p, int64_t cap_bytes, bool reverse) {
     pos[t] = start;
     end = e;
   }
+  if (end > INT64_MAX / 4) return fail(SBP_ERANGE, "sbp_bucket_plan: flat size overflows");
   const int64_t nb = end > 0 ? (end + size - 1) / size : (T > 0 ? 1 : 0);
-  if (nb > INT32_MAX) return fail(SBP_ERANGE, "sbp_bucket_plan: too many buckets");
+  if (nb > kMaxBuckets) return fail(SBP_ERANGE, "sbp_bucket_plan: more than 2^24 buckets");
   p->tensor_bucket.assign(T, 0);
   p->tensor_offset.assign(T, 0);
   for (int32_t t = 0; t < T; ++t) {
@@ -109,8 +114,8 @@ sbp_status split_plan(sbp_plan* p, int64_t cap_bytes, bool reverse) {
     k.chunk = k.padded / p->world_n;
     k.shard_offset = shard;
     k.flat_offset = lo;
-    shard += k.chunk;
-    flat += k.padded;
+    if (!add_ok(shard, k.chunk, &shard) || !add_ok(flat, k.padded, &flat))
+      return fail(SBP_ERANGE, "sbp_bucket_plan: total size overflows");
   }
   // members of each bucket, in visit order
   for (int32_t i = 0; i < T; ++i) {
@@ -258,9 +263,9 @@ sbp_status sbp_bucket_plan_per_tensor(const int64_t* numel, const int64_t* row_e
       const int64_t a = align_elems;
       int64_t g = a, r = row;
       while (r) { const int64_t q = g % r; g = r; r = q; }
-      const int64_t unit = a / g * row;
-      int64_t step;
-      if (unit <= 0 || __builtin_mul_overflow(unit, static_cast<int64_t>(world_n), &step)) {
+      int64_t unit, step;
+      if (__builtin_mul_overflow(a / g, row, &unit) ||
+          __builtin_mul_overflow(unit, static_cast<int64_t>(world_n), &step)) {
         delete p;
         return fail(SBP_ERANGE, "sbp_bucket_plan_per_tensor: row unit overflows");
       }

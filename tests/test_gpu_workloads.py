@@ -338,3 +338,100 @@ def test_tiny_mlp_zero_round_trip(split):
         want = OS.unpack(opl, OS.gather(opl, oshards))
         for tid in range(len(w.numels)):
             H.assert_bits_equal(H.to_np_u16(params[tid]), want[tid], f"step {t} tensor {tid}")
+
+
+def test_shard_union_resume_and_reshard():
+    """The invariants that make sharding safe, on the GPU path, bit for bit:
+    the union of the N = 4 shard updates equals the unsharded (N = 1) update,
+    resuming from a host copy of the shard state equals running on, and
+    resharding N = 4 -> 1 mid-run equals the unsharded run ("Distributed
+    Training and Parallelism", "Reproduction and debugging": resumability and
+    mesh reconfiguration).  A ragged model, so buckets carry padding; the
+    unsharded run is also checked against the oracle."""
+    import torch
+    numels = [1000, 37, 4096, 130, 8, 513, 2]
+    R, hp, sig = 3, sbp.AdamW(), 1e-2
+    scale = sbp.mean_scale(R)
+    theta = [synth.normal_f32(SEED, synth.master_stream(100 + t), k, 0.02)
+             for t, k in enumerate(numels)]
+
+    def layout(N):
+        return (sbp.bucket_plan(numels, 2048, N), OP.bucket_plan(numels, 2048, N))
+
+    def to_shards(opl, per_tensor):
+        """Per-tensor fp32 arrays -> each rank's shard (host), padding +0."""
+        flat = np.zeros(opl.flat_numel, np.float32)
+        for t, x in enumerate(per_tensor):
+            flat[opl.tensor_flat_offset(t):opl.tensor_flat_offset(t) + x.size] = x
+        return [OS.chunk(opl, flat, s) for s in range(opl.world_n)]
+
+    def to_tensors(opl, shards):
+        return [x.copy() for x in OS.unpack(opl, OS.gather(opl, shards))]
+
+    def upload(opl, tensors_th, tensors_m, tensors_v):
+        cols = [to_shards(opl, x) for x in (tensors_th, tensors_m, tensors_v)]
+        return [[H.from_np_f32(cols[i][s]) for i in range(3)] for s in range(opl.world_n)]
+
+    def download(opl, state):
+        return [to_tensors(opl, [H.to_np_f32(state[s][i]) for s in range(opl.world_n)])
+                for i in range(3)]
+
+    grads = [[H.empty_u16(k) for k in numels] for _ in range(R)]
+
+    def step(pl, state, t):
+        for r in range(R):
+            for tid in range(len(numels)):
+                synth.dev_normal_bf16(grads[r][tid], SEED, synth.tensor_stream(t, 0, r, tid), sig)
+        flats = [H.empty_u16(pl.flat_numel) for _ in range(R)]
+        for r in range(R):
+            sbp.pack_grads(pl, grads[r], flats[r])
+        for s in range(pl.world_n):
+            recv = [H.empty_u16(pl.shard_numel) for _ in range(R)]
+            for r in range(R):
+                sbp.shard_of(pl, s, flats[r], recv[r])
+            sbp.adamw_shard(recv, None, scale, *state[s], H.empty_u16(pl.shard_numel), hp, t)
+
+    zeros = [np.zeros(k, np.float32) for k in numels]
+    pl4, opl4 = layout(4)
+    pl1, opl1 = layout(1)
+    assert pl4.shard_numel * 4 > sum(numels)  # padding present
+    # unsharded: 6 steps
+    full = upload(opl1, theta, zeros, zeros)
+    for t in range(1, 7):
+        step(pl1, full, t)
+    torch.cuda.synchronize()
+    want = download(opl1, full)
+    # N = 4: 3 steps, state to the host and back (checkpoint), 3 more steps
+    sh = upload(opl4, theta, zeros, zeros)
+    for t in range(1, 4):
+        step(pl4, sh, t)
+    torch.cuda.synchronize()
+    ckpt = download(opl4, sh)
+    del sh
+    sh = upload(opl4, *ckpt)
+    for t in range(4, 7):
+        step(pl4, sh, t)
+    torch.cuda.synchronize()
+    got_resume = download(opl4, sh)
+    # N = 4 for 3 steps, resharded to N = 1 for the last 3
+    re = upload(opl1, *ckpt)
+    for t in range(4, 7):
+        step(pl1, re, t)
+    torch.cuda.synchronize()
+    got_reshard = download(opl1, re)
+    for name, got in (("resume", got_resume), ("reshard", got_reshard)):
+        for i, what in enumerate(("master", "m", "v")):
+            for t in range(len(numels)):
+                H.assert_bits_equal(got[i][t], want[i][t], f"{name} {what} tensor {t}")
+    # the unsharded GPU run against the oracle
+    th1 = to_shards(opl1, theta)[0]
+    m1 = np.zeros(pl1.shard_numel, np.float32)
+    v1 = m1.copy()
+    for t in range(1, 7):
+        gh = [[synth.normal_bf16(SEED, synth.tensor_stream(t, 0, r, tid), k, sig)
+               for tid, k in enumerate(numels)] for r in range(R)]
+        peers = [OS.chunk(opl1, OS.pack(opl1, g), 0) for g in gh]
+        th1, m1, v1, _ = OS.shard_step(peers, None, OS.mean_scale(R), th1, m1, v1, hp, t)
+    for i, x in enumerate((th1, m1, v1)):
+        for t, y in enumerate(to_tensors(opl1, [x])):
+            H.assert_bits_equal(want[i][t], y, f"unsharded vs oracle {i} tensor {t}")
