@@ -394,7 +394,8 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
  * sbp_clip_scale (host): with total_sq the sum of all ranks' squared norms,
  *   coef = min(1, max_norm / (sqrt(total_sq) + 1e-6)) in float64 (a NaN norm
  *   gives a NaN coefficient), *clipped_scale = fl32(scale * coef), and
- *   *coef (optional) receives coef.  Errors: SBP_EINVAL (null output).
+ *   *coef (optional) receives coef.  Errors: SBP_EINVAL (null output,
+ *   max_norm negative or NaN, total_sq negative).
  * ---------------------------------------------------------------------- */
 int64_t sbp_grad_sq_norm_workspace(int64_t n);
 sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R,

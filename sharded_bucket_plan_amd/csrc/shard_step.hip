@@ -932,6 +932,10 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale, float* clipped_scale,
                           double* coef) {
   if (clipped_scale == nullptr) return sbp::fail(SBP_EINVAL, "sbp_clip_scale: null output");
+  if (!(max_norm >= 0.0f))  // also rejects NaN
+    return sbp::fail(SBP_EINVAL, "sbp_clip_scale: max_norm must be >= 0");
+  if (total_sq < 0.0)  // a sum of squares; NaN is let through and propagates
+    return sbp::fail(SBP_EINVAL, "sbp_clip_scale: total_sq must be >= 0");
   const double q = static_cast<double>(max_norm) / (sqrt(total_sq) + 1e-6);
   const double c = (q < 1.0 || q != q) ? q : 1.0;  // NaN propagates
   *clipped_scale = static_cast<float>(static_cast<double>(scale) * c);

@@ -182,6 +182,10 @@ def test_clip_scale_matches_oracle():
     got, coef = sbp.clip_scale(float("nan"), 1.0, 0.5)
     assert math.isnan(coef) and math.isnan(got)
     assert sbp.clip_scale(float("inf"), 1.0, 0.5) == (0.0, 0.0)
+    assert sbp.clip_scale(4.0, 0.0, 0.5) == (0.0, 0.0)  # max_norm 0 zeroes the update
+    for bad in ((1.0, -1.0), (1.0, float("nan")), (-1.0, 1.0)):
+        with pytest.raises(sbp.SbpError):
+            sbp.clip_scale(bad[0], bad[1], 0.5)
 
 
 def test_grad_sq_norm_validates_before_launch():
