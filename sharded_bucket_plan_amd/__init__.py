@@ -7,9 +7,14 @@ the current HIP stream.  There is no fallback: if libsbp.so is missing, or a
 call fails, an error is raised.
 
 Functions (same names as the C calls without the "sbp_" prefix):
-  bucket_plan, pack_grads, unpack_params, shard_of, gather_shards,
-  reduce_shard, accumulate_grads, adamw_shard, mean_scale, tokens_scale,
-  grad_sq_norm, clip_scale.
+  plans        bucket_plan (whole-tensor or split buckets), bucket_plan_per_tensor
+               (one bucket per tensor, dim-0 row shards), Plan queries
+  layout       pack_grads, unpack_params, shard_of, gather_shards
+  scales       mean_scale, tokens_scale, clip_scale
+  shard step   reduce_shard, accumulate_grads, adamw_shard, grad_sq_norm
+               (+ grad_sq_norm_workspace)
+  groups       group_runs (+ group_table: the run table on a device),
+               adamw_shard_grouped
 """
 
 import ctypes
