@@ -453,6 +453,59 @@ def bucket_sweep(seed, reps=5):
     return {"bucket_sweep": rows, "fit": fit, "bytes_per_pass": M, "shard_numel": n}
 
 
+def layout_moves(seed, reps=5):
+    """The layout calls at Llama-3-8B scale (N = 8, 162 buckets of 291 tensors,
+    8,030,261,248 elements): rank 0's chunks of one rank's flat buckets
+    (shard_of: what that rank contributes to owner 0 in the reduce-scatter),
+    the 8 shards into the flat buckets (gather_shards: the all-gather's
+    layout), and the flat buckets into the 291 per-tensor parameters
+    (unpack_params), as well as pack_grads (per-tensor gradients into the
+    buckets).  Each call is timed with events on the launch stream, median of
+    `reps`; algorithmic bytes are one read and one write per element moved
+    (a zero-filled padding element is a write only)."""
+    import statistics as st
+    import torch
+    import sharded_bucket_plan_amd as sbp
+    import synth
+
+    w = synth.WORKLOADS["llama3_8b"]
+    dev = torch.device("cuda:0")
+    pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    n, F, P = pl.shard_numel, pl.flat_numel, sum(w.numels)
+    flat = torch.empty(F, dtype=torch.int16, device=dev)
+    shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
+                                    synth.peer_stream(1, 0, r), w.grad_sigma)
+              for r in range(w.world_n)]
+    tensors = [torch.empty(k, dtype=torch.int16, device=dev) for k in w.numels]
+    for t, x in enumerate(tensors):
+        synth.dev_normal_bf16(x, seed, synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
+    calls = {
+        "pack_grads": (lambda: sbp.pack_grads(pl, tensors, flat), 4 * P + 2 * (F - P)),
+        "shard_of": (lambda: sbp.shard_of(pl, 0, flat, shards[0]), 4 * n),
+        "gather_shards": (lambda: sbp.gather_shards(pl, shards, flat), 4 * F),
+        "unpack_params": (lambda: sbp.unpack_params(pl, flat, tensors), 4 * P),
+    }
+    out = {}
+    for name, (f, nbytes) in calls.items():
+        f()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        med = st.median(ms)
+        out[name] = {"ms_median": med, "ms_min": min(ms), "algorithmic_bytes": nbytes,
+                     "gbs": nbytes / (med * 1e-3) / 1e9,
+                     "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_GBS}
+        log(f"layout: {name} {med:.3f} ms {out[name]['gbs']:.0f} GB/s")
+    return {"layout_moves": out, "workload": "llama3_8b", "N": w.world_n, "shard_numel": n,
+            "flat_numel": F, "tensors": len(w.numels), "buckets": pl.num_buckets}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,6 +523,9 @@ def main():
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--bucket-sweep", action="store_true",
                     help="only run the bucket-size sweep (7.5B shard) and print its JSON")
+    ap.add_argument("--layout", action="store_true",
+                    help="only time the layout calls (pack, shard_of, gather, unpack) at "
+                         "Llama-3-8B scale and print their JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5,
@@ -495,6 +551,9 @@ def main():
         sys.exit(1)
     if args.bucket_sweep:
         print(json.dumps(bucket_sweep(seed)), flush=True)
+        return
+    if args.layout:
+        print(json.dumps(layout_moves(seed)), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
