@@ -277,6 +277,49 @@ def test_special_values():
     assert np.array_equal(np.isnan(H.to_np_f32(out)), np.isnan(S))
 
 
+HP_EDGES = [
+    ("lr 0", sbp.AdamW(0.0, 0.9, 0.999, 1e-8, 0.01), (1, 2)),
+    ("wd 0", sbp.AdamW(1e-3, 0.9, 0.999, 1e-8, 0.0), (1, 2)),
+    ("betas 0", sbp.AdamW(1e-3, 0.0, 0.0, 1e-8, 0.01), (1, 2)),
+    ("big lr and wd", sbp.AdamW(1.0, 0.9, 0.999, 1e-8, 2.0), (1, 2)),
+    ("late steps", sbp.AdamW(), (1000, 1001)),
+    ("very late steps", sbp.AdamW(), (10 ** 6, 10 ** 6 + 1)),
+    ("eps 0, zero grads", sbp.AdamW(1e-3, 0.9, 0.999, 0.0, 0.01), (1, 2)),
+]
+
+
+@pytest.mark.parametrize("name,hp,steps", HP_EDGES, ids=[e[0] for e in HP_EDGES])
+def test_adamw_hyperparameter_edges(name, hp, steps):
+    """Edge hyperparameters (learning rate or decay 0, betas 0, decay factor
+    below 0, bias corrections saturated at late steps, eps 0 over zero
+    gradients, which makes 0/0) through two steps, against the oracle."""
+    import torch
+    n, R = 2 * 2048 + 13, 3
+    th, m, v = _state(18, n)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    dp = H.empty_u16(n)
+    zero = name.startswith("eps 0")
+    want = (th, m, v, None)
+    for t in steps:
+        if zero:
+            ph = [np.zeros(n, np.uint16) for _ in range(R)]
+            dpe = [H.from_np_u16(x) for x in ph]
+        else:
+            ph = H.host_peers(18, t, 0, R, n, 1e-3)
+            dpe = H.dev_peers(18, t, 0, R, n, 1e-3)
+        sbp.adamw_shard(dpe, None, sbp.mean_scale(R), dth, dm, dv, dp, hp, t)
+        with np.errstate(all="ignore"):
+            want = OS.shard_step(ph, None, OS.mean_scale(R), want[0], want[1], want[2], hp, t)
+    torch.cuda.synchronize()
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    if zero:  # every update is 0/0: NaN on both sides (payload signs may differ)
+        assert np.all(np.isnan(got[0])) and np.all(np.isnan(want[0]))
+        assert H.assert_state_close(got, want, name) == 0
+    else:
+        for a, b, what in zip(got, want, ("master", "m", "v", "param")):
+            H.assert_bits_equal(a, b, f"{name} {what}")
+
+
 # ---- pack --------------------------------------------------------------------
 
 def _pack_case(numels, cap, N, align=8, misalign=False, seed=3):
