@@ -198,6 +198,33 @@ def test_adamw_shard_grouped(R, n):
     assert H.canaries_intact(pw, g)
 
 
+def test_adamw_shard_grouped_eight_groups():
+    """All SBP_MAX_GROUPS groups in use, each with its own lr and decay;
+    runs of every length from 1 element to several tiles."""
+    import torch
+    groups = [(1e-3 * (k + 1), 0.01 * k) for k in range(sbp.MAX_GROUPS)]
+    n = 9 * 2048 + 5
+    rng = np.random.default_rng(19)
+    cuts = np.unique(rng.integers(1, n, 60))
+    starts = np.r_[0, cuts].astype(np.int64)
+    ids = (np.arange(starts.size) % sbp.MAX_GROUPS).astype(np.int32)
+    eg = np.repeat(ids, np.diff(np.r_[starts, n])).astype(np.int64)
+    th, m, v = _state(19, n)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    dp = H.empty_u16(n)
+    rs, rg = torch.from_numpy(starts).to(H.dev()), torch.from_numpy(ids).to(H.dev())
+    peers = H.dev_peers(19, 1, 0, 4, n, 1e-3)
+    sbp.adamw_shard_grouped(peers, None, 0.25, dth, dm, dv, dp, HP, 1, groups, rs, rg)
+    torch.cuda.synchronize()
+    want = OS.shard_step_grouped(H.host_peers(19, 1, 0, 4, n, 1e-3), None, np.float32(0.25),
+                                 th, m, v, HP, groups, eg, 1)
+    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
+        H.assert_bits_equal(a, b, f"eight groups {name}")
+    with pytest.raises(ValueError):
+        sbp.adamw_shard_grouped(peers, None, 0.25, dth, dm, dv, dp, HP, 1, groups * 2, rs, rg)
+
+
 def test_adamw_shard_grouped_one_group_is_plain():
     """One run of one group: the grouped step equals the plain step."""
     import torch
