@@ -582,9 +582,16 @@ def test_grouped_matches_torch_param_groups():
 
 
 def test_shard_groups_follow_tensors_and_padding():
-    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3]
-    pl = P.bucket_plan(numels, 600, 4)
-    tg = [t % 3 for t in range(len(numels))]
+    # the second and third plans leave whole shards of padding (tensor 0
+    # alone in a 32-element bucket), so a shard can start with padding
+    for numels, cap, tg in (([37, 8, 1, 130, 0, 64, 9, 250, 3], 600, None),
+                            ([3, 5], 2, [2, 1]), ([3], 1 << 20, [1])):
+        _check_shard_groups(numels, cap, tg)
+
+
+def _check_shard_groups(numels, cap, tg):
+    pl = P.bucket_plan(numels, cap, 4)
+    tg = tg or [t % 3 for t in range(len(numels))]
     for s in range(4):
         g = S.shard_groups(pl, s, tg)
         flat_ids = S.chunk(pl, np.arange(pl.flat_numel), s)
