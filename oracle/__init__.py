@@ -15,11 +15,15 @@ operation (numpy float32 ufuncs: one rounding each, no fused multiply-add,
 subnormals kept), and host scalars in float64 rounded once to binary32.
 
 Modules:
-  plan   bucket plan: per-tensor offsets in flat buckets, padding, per-rank
-         chunks, shard map, model-state byte accounting
-  step   pack / chunk / gather, ascending-rank reduce, accumulate, normalise,
-         AdamW, bf16 cast, the whole shard step composed from them, and
-         global gradient-norm clipping (squared norm, coefficient, scale)
+  plan   bucket plans -- whole tensors per bucket, fixed-size buckets with
+         tensors split across them, one bucket per tensor with dim-0 row
+         shards -- with per-tensor offsets, padding, per-rank chunks, the
+         shard map and model-state byte accounting
+  step   pack / unpack / chunk / gather, ascending-rank reduce, accumulate,
+         normalise, AdamW, bf16 cast, the whole shard step composed from
+         them, global gradient-norm clipping (squared norm, coefficient,
+         scale), and parameter groups (per-element groups of a shard, the
+         grouped step)
 
 Every function is pinned by tests/test_oracle_*.py against closed forms,
 invariants, special cases, library routines or brute force; none is
