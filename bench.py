@@ -18,6 +18,14 @@ HBM:
                 into 162 buckets + the fused step over 8.03B elements
 value = shard elements updated per second (whole job = the one GPU).
 
+Variants of the step (same JSON line): --clip MAX_NORM adds global-norm
+clipping (the norm pass writing G, then the update from G); --groups uses
+two parameter groups (no weight decay on 1-D tensors) and the grouped step.
+Other modes print their own JSON: --layout times pack / shard_of /
+gather_shards / unpack_params at Llama-3-8B scale; --bucket-sweep times one
+accumulate pass per bucket for caps of 1..256 MiB on the 7.5B shard;
+--calibrate-copy and --summarize-pmc make the HBM-counter summary.
+
 The roofline object is for the fused kernel: algorithmic bytes per launch
 ((26 + 2R) bytes per element, +4 with an fp32 accumulator) over its average
 launch time, measured with HIP events on the stream it is launched on.
