@@ -560,8 +560,11 @@ def test_layout_moves(kind, misalign):
 
 def test_graph_capture_replays():
     """The calls allocate nothing and pass their tables by value, so a step can
-    be captured in a HIP graph.  Each replay starts from the same saved state
-    (restored by eager copies between replays) and must equal the eager run."""
+    be captured in a HIP graph.  The captured step uses every device entry
+    point: pack, shard_of, accumulate, reduce, the squared norm, the fused
+    step from G, the grouped fused step, gather and unpack.  Each replay
+    starts from the same saved state (restored by eager copies between
+    replays) and must equal the eager run."""
     import torch
     numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
     pl = sbp.bucket_plan(numels, 600, 1)
@@ -570,6 +573,7 @@ def test_graph_capture_replays():
     grads = [H.from_np_u16(synth.normal_bf16(41, synth.tensor_stream(1, 0, 0, t), k, 1e-2))
              if k else H.empty_u16(0) for t, k in enumerate(numels)]
     flat = H.empty_u16(n)
+    shard = H.empty_u16(n)
     other = H.from_np_u16(synth.normal_bf16(41, synth.peer_stream(1, 0, 1), n, 1e-2))
     mb0 = [H.from_np_u16(synth.normal_bf16(41, synth.peer_stream(1, 1, r), n, 1e-2))
            for r in range(R)]
@@ -577,24 +581,48 @@ def test_graph_capture_replays():
     init = [H.from_np_f32(th0), H.from_np_f32(np.zeros(n, np.float32)),
             H.from_np_f32(np.zeros(n, np.float32))]
     work = [x.clone() for x in init]
+    work2 = [x.clone() for x in init]
     acc = torch.empty(n, dtype=torch.float32, device=H.dev())
     gsum = torch.empty(n, dtype=torch.float32, device=H.dev())
+    red = torch.empty(n, dtype=torch.float32, device=H.dev())
     p = H.empty_u16(n)
+    p2 = H.empty_u16(n)
+    gathered = H.empty_u16(n)
+    params = [H.empty_u16(k) for k in numels]
     ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=H.dev())
     sq = torch.empty(1, dtype=torch.float64, device=H.dev())
     scale = sbp.mean_scale(R, 2)
+    groups = [(1e-3, 0.1), (5e-4, 0.0)]
+    rs, rg = sbp.group_table(pl, 0, [t % 2 for t in range(len(numels))], H.dev())
 
     def step():
         sbp.pack_grads(pl, grads, flat)
+        sbp.shard_of(pl, 0, flat, shard)
         sbp.accumulate_grads(acc, mb0, first=True)
-        sbp.grad_sq_norm([flat, other], acc, scale, n, g_sum_out=gsum, workspace=ws, sq_out=sq)
+        sbp.reduce_shard([shard, other], scale, red)
+        sbp.grad_sq_norm([shard, other], acc, scale, n, g_sum_out=gsum, workspace=ws, sq_out=sq)
         sbp.adamw_shard([], gsum, scale, *work, p, HP, 1)
+        sbp.adamw_shard_grouped([shard, other], acc, scale, *work2, p2, HP, 1, groups, rs, rg)
+        sbp.gather_shards(pl, [p2], gathered)
+        sbp.unpack_params(pl, gathered, params)
 
+    outs = lambda: work + work2 + [p, p2, sq, red, gathered] + params
+    names = (["master", "m", "v", "grouped master", "grouped m", "grouped v", "param",
+              "grouped param", "sq", "reduced", "gathered"] +
+             [f"param tensor {t}" for t in range(len(numels))])
     step()
     torch.cuda.synchronize()
-    eager = [x.clone() for x in work] + [p.clone(), sq.clone()]
-    for x, y in zip(work, init):
-        x.copy_(y)
+    eager = [x.clone() for x in outs()]
+
+    def reset():
+        for x, y in zip(work + work2, init + init):
+            x.copy_(y)
+        for x in (p, p2, gathered, *params):
+            x.fill_(0)
+        for x in (sq, red):
+            x.fill_(-1.0)
+
+    reset()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm-up on the side stream, as capture expects
@@ -605,13 +633,9 @@ def test_graph_capture_replays():
     with torch.cuda.graph(g):
         step()
     for _ in range(4):
-        for x, y in zip(work, init):
-            x.copy_(y)
-        p.fill_(0)
-        sq.fill_(-1.0)
+        reset()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [x for x in work] + [p, sq]
-        for a, b, name in zip(got, eager, ("master", "m", "v", "param", "sq")):
+        for a, b, name in zip(outs(), eager, names):
             assert torch.equal(a, b), f"graph replay differs in {name}"
