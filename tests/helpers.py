@@ -117,8 +117,20 @@ def guarded(n, itemsize, guard=64, fill=0x5A):
     g = max(guard, 16)
     whole = torch.full((n * itemsize + 2 * g,), fill, dtype=torch.uint8, device=dev())
     inner = whole[g:g + n * itemsize]
-    dt = {2: torch.int16, 4: torch.float32}[itemsize]
+    dt = {2: torch.int16, 4: torch.float32, 8: torch.float64}[itemsize]
     return whole, inner.view(dt), g
+
+
+def guarded_from(a):
+    """guarded() holding a copy of the numpy array `a` (float32, or uint16 bf16
+    bits)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    whole, inner, g = guarded(a.size, a.dtype.itemsize)
+    if a.size:
+        src = a.view(np.int16) if a.dtype.itemsize == 2 else a
+        inner.copy_(torch.from_numpy(src).to(dev()))
+    return whole, inner, g
 
 
 def canaries_intact(whole, g, fill=0x5A):

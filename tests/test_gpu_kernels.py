@@ -72,7 +72,7 @@ def test_reduce_shard_big_multi_pass():
 def test_accumulate_grads(R, n):
     import torch
     K = 3
-    acc = torch.empty(n, dtype=torch.float32, device=H.dev())
+    whole, acc, g = H.guarded(n, 4)
     bufs = None
     A = None
     for k in range(K):
@@ -81,6 +81,7 @@ def test_accumulate_grads(R, n):
         A = OS.accumulate(A, OS.reduce_peers(H.host_peers(13, 2, k, R, n, 1e-3)))
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_f32(acc), A, f"accumulate R={R} n={n}")
+    assert H.canaries_intact(whole, g)
 
 
 def _state(seed, n):
@@ -97,7 +98,8 @@ def test_adamw_shard(R, n, with_acc):
         pytest.skip("big size runs at R=8 only")
     steps = 3
     th, m, v = _state(14, n)
-    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    gs = [H.guarded_from(x) for x in (th, m, v)]
+    dth, dm, dv = (x[1] for x in gs)
     pw, dp, g = H.guarded(n, 2)
     bufs = None
     acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if with_acc else None
@@ -118,6 +120,7 @@ def test_adamw_shard(R, n, with_acc):
     worst = H.assert_state_close(got, want, f"adamw R={R} n={n} acc={with_acc}")
     assert worst == 0, f"expected bit-exact, worst {worst} ulp"
     assert H.canaries_intact(pw, g)
+    assert all(H.canaries_intact(w, gg) for w, _, gg in gs)
 
 
 def test_adamw_shard_acc_only():
@@ -174,7 +177,8 @@ def test_adamw_shard_grouped(R, n):
     eg = _elem_groups(starts, groups, n)
     rs, rg = torch.from_numpy(starts).to(H.dev()), torch.from_numpy(groups).to(H.dev())
     th, m, v = _state(16, n)
-    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(m), H.from_np_f32(v)
+    gs = [H.guarded_from(x) for x in (th, m, v)]
+    dth, dm, dv = (x[1] for x in gs)
     pw, dp, g = H.guarded(n, 2)
     acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if R == 0 else None
     want = (th, m, v, None)
@@ -196,6 +200,7 @@ def test_adamw_shard_grouped(R, n):
     for a, b, name in zip(got, want, ("master", "m", "v", "param")):
         H.assert_bits_equal(a, b, f"grouped R={R} n={n} {name}")
     assert H.canaries_intact(pw, g)
+    assert all(H.canaries_intact(w, gg) for w, _, gg in gs)
 
 
 def test_adamw_shard_grouped_eight_groups():
@@ -430,9 +435,13 @@ def test_grad_sq_norm(R, n, write):
         acc_h = OS.reduce_peers(H.host_peers(21, 1, 1, 2, n, 1e-3))
     scale = sbp.mean_scale(max(R, 1), 2)
     whole, gsum, g = H.guarded(n, 4)
-    sq = sbp.grad_sq_norm(bufs, acc_d, scale, n, g_sum_out=gsum if write else None)
+    ws_whole, ws, ws_g = H.guarded(sbp.grad_sq_norm_workspace(n), 8)
+    sq_whole, sq_out, sq_g = H.guarded(1, 8)
+    sq = sbp.grad_sq_norm(bufs, acc_d, scale, n, g_sum_out=gsum if write else None,
+                          workspace=ws, sq_out=sq_out)
     sq2 = sbp.grad_sq_norm(bufs, acc_d, scale, n)
     torch.cuda.synchronize()
+    assert H.canaries_intact(ws_whole, ws_g) and H.canaries_intact(sq_whole, sq_g)
     if R:
         S = OS.reduce_peers(H.host_peers(21, 1, 0, R, n, 1e-3))
         G = S if acc_h is None else acc_h + S
@@ -505,16 +514,23 @@ def test_layout_moves(kind, misalign):
         opl = OP.bucket_plan(numels, 600, N, split=kind == "split")
     grads_h = [synth.normal_bf16(31, synth.tensor_stream(1, 0, 0, t), n, 1e-2)
                for t, n in enumerate(numels)]
-    keep = []
+    bases = []  # (base, view start, length): everything outside the view must stay 0x5A5A
 
     def dev_tensor(h):
-        if misalign and h.size:
-            base = torch.empty(h.size + 5, dtype=torch.int16, device=H.dev())
-            keep.append(base)
-            v = base[5:]
+        lead = 5 if misalign else 8
+        base = torch.full((h.size + lead + 64,), 0x5A5A, dtype=torch.int16, device=H.dev())
+        v = base[lead:lead + h.size]
+        if h.size:
             v.copy_(H.from_np_u16(h))
-            return v
-        return H.from_np_u16(h) if h.size else H.empty_u16(0)
+        bases.append((base, lead, h.size))
+        return v
+
+    def guards_ok():
+        for base, lead, k in bases:
+            b = H.to_np_u16(base)
+            if not (np.all(b[:lead] == 0x5A5A) and np.all(b[lead + k:] == 0x5A5A)):
+                return False
+        return True
 
     gd = [dev_tensor(h) for h in grads_h]
     flat = H.empty_u16(pl.flat_numel)
@@ -533,17 +549,20 @@ def test_layout_moves(kind, misalign):
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_u16(flat2), want_flat, "pack by bucket")
     # shard_of each rank, then gather back
-    shards = [H.empty_u16(pl.shard_numel) for _ in range(N)]
+    shard_g = [H.guarded(pl.shard_numel, 2) for _ in range(N)]
+    shards = [x[1] for x in shard_g]
     for s in range(N):
         sbp.shard_of(pl, s, flat, shards[s])
     torch.cuda.synchronize()
     for s in range(N):
         H.assert_bits_equal(H.to_np_u16(shards[s]), OS.chunk(opl, want_flat, s), f"shard {s}")
-    back = H.empty_u16(pl.flat_numel)
+    assert all(H.canaries_intact(w, gg) for w, _, gg in shard_g)
+    back_whole, back, back_g = H.guarded(pl.flat_numel, 2)
     back.fill_(0x1234)
     sbp.gather_shards(pl, shards, back)
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_u16(back), want_flat, "gather")
+    assert H.canaries_intact(back_whole, back_g)
     # unpack into per-tensor buffers (all at once, and bucket by bucket)
     outs = [dev_tensor(np.zeros(n, np.uint16)) for n in numels]
     sbp.unpack_params(pl, back, outs)
@@ -556,6 +575,7 @@ def test_layout_moves(kind, misalign):
     for t, h in enumerate(grads_h):
         H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack tensor {t}")
         H.assert_bits_equal(H.to_np_u16(outs2[t]), h, f"unpack by bucket, tensor {t}")
+    assert guards_ok(), "a write outside a per-tensor buffer"
 
 
 def test_graph_capture_replays():
