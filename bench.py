@@ -510,8 +510,24 @@ def layout_moves(seed, reps=5):
                      "gbs": nbytes / (med * 1e-3) / 1e9,
                      "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_GBS}
         log(f"layout: {name} {med:.3f} ms {out[name]['gbs']:.0f} GB/s")
-    return {"layout_moves": out, "workload": "llama3_8b", "N": w.world_n, "shard_numel": n,
-            "flat_numel": F, "tensors": len(w.numels), "buckets": pl.num_buckets}
+    # the plans themselves (host only, made once per model): microseconds per build
+    plans = {}
+    rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
+    for name, make in (("bucket_plan", lambda: sbp.bucket_plan(w.numels, w.bucket_cap_bytes,
+                                                                w.world_n)),
+                       ("bucket_plan split", lambda: sbp.bucket_plan(w.numels, w.bucket_cap_bytes,
+                                                                      w.world_n, split=True)),
+                       ("bucket_plan_per_tensor", lambda: sbp.bucket_plan_per_tensor(
+                           w.numels, w.world_n, rows))):
+        make()
+        t0 = time.perf_counter()
+        for _ in range(200):
+            make()
+        plans[name] = {"us_per_plan": (time.perf_counter() - t0) / 200 * 1e6}
+        log(f"layout: {name} {plans[name]['us_per_plan']:.1f} us per plan")
+    return {"layout_moves": out, "plans": plans, "workload": "llama3_8b", "N": w.world_n,
+            "shard_numel": n, "flat_numel": F, "tensors": len(w.numels),
+            "buckets": pl.num_buckets}
 
 
 def main():
