@@ -22,7 +22,7 @@ Variants of the step (same JSON line): --clip MAX_NORM adds global-norm
 clipping (the norm pass writing G, then the update from G); --groups uses
 two parameter groups (no weight decay on 1-D tensors) and the grouped step.
 Other modes print their own JSON: --layout times pack / shard_of /
-gather_shards / unpack_params at Llama-3-8B scale; --bucket-sweep times one
+gather_shards / unpack_params and the plan builds on the workload's model; --bucket-sweep times one
 accumulate pass per bucket for caps of 1..256 MiB on the 7.5B shard;
 --calibrate-copy and --summarize-pmc make the HBM-counter summary.
 
@@ -461,22 +461,24 @@ def bucket_sweep(seed, reps=5):
     return {"bucket_sweep": rows, "fit": fit, "bytes_per_pass": M, "shard_numel": n}
 
 
-def layout_moves(seed, reps=5):
-    """The layout calls at Llama-3-8B scale (N = 8, 162 buckets of 291 tensors,
-    8,030,261,248 elements): rank 0's chunks of one rank's flat buckets
+def layout_moves(seed, workload="llama3_8b", reps=5):
+    """The layout calls on a workload's model (default Llama-3-8B at N = 8:
+    162 buckets of 291 tensors, 8,030,261,248 elements): rank 0's chunks of one rank's flat buckets
     (shard_of: what that rank contributes to owner 0 in the reduce-scatter),
     the 8 shards into the flat buckets (gather_shards: the all-gather's
     layout), and the flat buckets into the 291 per-tensor parameters
     (unpack_params), as well as pack_grads (per-tensor gradients into the
     buckets).  Each call is timed with events on the launch stream, median of
-    `reps`; algorithmic bytes are one read and one write per element moved
-    (a zero-filled padding element is a write only)."""
+    `reps`, twice: as a Python call (host marshalling included) and as a
+    replay of a graph holding the call's launches k times (GPU time, which
+    the roofline figures use; k spreads the graph's own launch cost); algorithmic bytes are one read and one write per element
+    moved (a zero-filled padding element is a write only)."""
     import statistics as st
     import torch
     import sharded_bucket_plan_amd as sbp
     import synth
 
-    w = synth.WORKLOADS["llama3_8b"]
+    w = synth.WORKLOADS[workload]
     dev = torch.device("cuda:0")
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n, F, P = pl.shard_numel, pl.flat_numel, sum(w.numels)
@@ -493,23 +495,44 @@ def layout_moves(seed, reps=5):
         "gather_shards": (lambda: sbp.gather_shards(pl, shards, flat), 4 * F),
         "unpack_params": (lambda: sbp.unpack_params(pl, flat, tensors), 4 * P),
     }
-    out = {}
-    for name, (f, nbytes) in calls.items():
-        f()
-        torch.cuda.synchronize()
+    def timed(run):
         ms = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            f()
+            run()
             b.record()
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
-        med = st.median(ms)
-        out[name] = {"ms_median": med, "ms_min": min(ms), "algorithmic_bytes": nbytes,
+        return st.median(ms)
+
+    out = {}
+    for name, (f, nbytes) in calls.items():
+        f()
+        torch.cuda.synchronize()
+        call = timed(f)  # the Python call as a user makes it, host marshalling included
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        # the same launches captured k times in one graph and replayed: GPU time,
+        # with the graph's own launch cost spread over k calls
+        k = max(1, min(50, int(2.0 / max(call, 1e-3))))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(k):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        med = timed(g.replay) / k
+        del g
+        out[name] = {"ms_median": med, "call_ms_median": call, "algorithmic_bytes": nbytes,
                      "gbs": nbytes / (med * 1e-3) / 1e9,
                      "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_GBS}
-        log(f"layout: {name} {med:.3f} ms {out[name]['gbs']:.0f} GB/s")
+        log(f"layout: {name} {med:.3f} ms on the GPU ({out[name]['gbs']:.0f} GB/s), "
+            f"{call:.3f} ms per Python call")
     # the plans themselves (host only, made once per model): microseconds per build
     plans = {}
     rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
@@ -525,7 +548,7 @@ def layout_moves(seed, reps=5):
             make()
         plans[name] = {"us_per_plan": (time.perf_counter() - t0) / 200 * 1e6}
         log(f"layout: {name} {plans[name]['us_per_plan']:.1f} us per plan")
-    return {"layout_moves": out, "plans": plans, "workload": "llama3_8b", "N": w.world_n,
+    return {"layout_moves": out, "plans": plans, "workload": workload, "N": w.world_n,
             "shard_numel": n, "flat_numel": F, "tensors": len(w.numels),
             "buckets": pl.num_buckets}
 
@@ -548,8 +571,8 @@ def main():
     ap.add_argument("--bucket-sweep", action="store_true",
                     help="only run the bucket-size sweep (7.5B shard) and print its JSON")
     ap.add_argument("--layout", action="store_true",
-                    help="only time the layout calls (pack, shard_of, gather, unpack) at "
-                         "Llama-3-8B scale and print their JSON")
+                    help="only time the layout calls (pack, shard_of, gather, unpack) and the "
+                         "plan builds on --workload's model and print their JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5,
@@ -577,7 +600,7 @@ def main():
         print(json.dumps(bucket_sweep(seed)), flush=True)
         return
     if args.layout:
-        print(json.dumps(layout_moves(seed)), flush=True)
+        print(json.dumps(layout_moves(seed, args.workload)), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
