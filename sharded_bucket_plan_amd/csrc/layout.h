@@ -14,8 +14,7 @@ namespace sbp {
 struct Seg {
   const uint16_t* src;
   uint16_t* dst;
-  int64_t len;          // elements
-  int64_t first_chunk;  // chunk index (within one launch) of the segment's start
+  int64_t len;  // elements
 };
 
 // Validate one layout call's arguments and list its copies in `segs`

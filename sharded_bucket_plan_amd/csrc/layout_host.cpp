@@ -98,11 +98,11 @@ sbp_status pack_segments(const sbp_plan* plan, int32_t bucket, const void* const
         return sbp::fail(SBP_EALIGN, "sbp_pack_grads: gradients must be 2-byte aligned");
       if (sbp::overlaps(src, 2 * plan->numel[pc.t], flat, 2 * plan->flat_numel))
         return sbp::fail(SBP_EINVAL, "sbp_pack_grads: a gradient overlaps the flat buffer");
-      if (pc.flat > pos) segs.push_back(Seg{nullptr, F + pos, pc.flat - pos, 0});
-      segs.push_back(Seg{static_cast<const uint16_t*>(src) + pc.elem, F + pc.flat, pc.len, 0});
+      if (pc.flat > pos) segs.push_back(Seg{nullptr, F + pos, pc.flat - pos});
+      segs.push_back(Seg{static_cast<const uint16_t*>(src) + pc.elem, F + pc.flat, pc.len});
       pos = pc.flat + pc.len;
     }
-    if (hi > pos) segs.push_back(Seg{nullptr, F + pos, hi - pos, 0});
+    if (hi > pos) segs.push_back(Seg{nullptr, F + pos, hi - pos});
   } catch (...) {
     return sbp::fail(SBP_ENOMEM, "sbp_pack_grads: out of host memory");
   }
@@ -140,7 +140,7 @@ sbp_status unpack_segments(const sbp_plan* plan, int32_t bucket, const void* fla
       if (pc.t != last)
         outs.push_back({reinterpret_cast<uintptr_t>(dst), 2 * plan->numel[pc.t]});
       last = pc.t;
-      segs.push_back(Seg{F + pc.flat, static_cast<uint16_t*>(dst) + pc.elem, pc.len, 0});
+      segs.push_back(Seg{F + pc.flat, static_cast<uint16_t*>(dst) + pc.elem, pc.len});
     }
     if (!disjoint(outs))
       return sbp::fail(SBP_EINVAL, "sbp_unpack_params: parameter buffers overlap");
@@ -174,7 +174,7 @@ sbp_status shard_of_segments(const sbp_plan* plan, int32_t bucket, int32_t rank,
     for (int32_t b = b0; b < b1; ++b) {
       const sbp::Bucket& k = plan->buckets[b];
       if (k.chunk > 0)
-        segs.push_back(Seg{F + k.flat_offset + rank * k.chunk, S + k.shard_offset, k.chunk, 0});
+        segs.push_back(Seg{F + k.flat_offset + rank * k.chunk, S + k.shard_offset, k.chunk});
     }
   } catch (...) {
     return sbp::fail(SBP_ENOMEM, "sbp_shard_of: out of host memory");
@@ -210,7 +210,7 @@ sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* con
       if (k.chunk == 0) continue;
       for (int32_t s = 0; s < plan->world_n; ++s)
         segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + k.shard_offset,
-                           F + k.flat_offset + s * k.chunk, k.chunk, 0});
+                           F + k.flat_offset + s * k.chunk, k.chunk});
     }
   } catch (...) {
     return sbp::fail(SBP_ENOMEM, "sbp_gather_shards: out of host memory");

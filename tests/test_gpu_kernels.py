@@ -407,14 +407,63 @@ def test_pack_one_bucket_at_a_time():
 
 
 def test_pack_big_tensors_many_launches():
-    """More segments than one launch carries, and chunks of multi-MB tensors."""
+    """More segments than one launch carries (160), and chunks of multi-MB tensors."""
     import torch
-    numels = [4096, 3 * 2 ** 20 + 8, 1000] * 40 + [5]
+    numels = [4096, 3 * 2 ** 20 + 8, 1000] * 60 + [5]
     pl, opl, gh, gd, keep = _pack_case(numels, 1 << 20, 8)
     flat = H.empty_u16(pl.flat_numel)
     sbp.pack_grads(pl, gd, flat)
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_u16(flat), OS.pack(opl, gh), "pack big")
+
+
+def test_layout_segment_longer_than_2_30():
+    """A tensor of more than 2^30 elements: its copy segment is split into
+    pieces for the kernel (whose segment length is 32-bit).  Pack, unpack and
+    shard_of are checked at sampled positions around every piece boundary
+    and at random, against the generator's values recomputed on the host."""
+    import torch
+    big = (1 << 30) + 12345
+    numels = [7, big, 3]
+    pl = sbp.bucket_plan(numels, 1 << 20, 2)
+    opl = OP.bucket_plan(numels, 1 << 20, 2)
+    dev = H.dev()
+    st = [synth.tensor_stream(1, 0, 0, t) for t in range(3)]
+    grads = [synth.dev_normal_bf16(torch.empty(k, dtype=torch.int16, device=dev), 42, st[t], 1e-2)
+             for t, k in enumerate(numels)]
+    flat = torch.full((pl.flat_numel,), 0x3333, dtype=torch.int16, device=dev)
+    sbp.pack_grads(pl, grads, flat)
+    rng = np.random.default_rng(43)
+    edges = [0, 1, (1 << 30) - 1, 1 << 30, (1 << 30) + 1, big - 2, big - 1]
+    idx = np.unique(np.r_[edges, rng.integers(0, big, 1 << 14)]).astype(np.int64)
+    want = synth.normal_bf16_at(42, st[1], idx, 1e-2)
+
+    def at(t, i):
+        return H.to_np_u16(t.index_select(0, torch.from_numpy(i).to(dev)))
+
+    off = opl.tensor_flat_offset(1)
+    H.assert_bits_equal(at(flat, off + idx), want, "pack of the big tensor")
+    for t in (0, 2):  # the small tensors land whole
+        o = opl.tensor_flat_offset(t)
+        H.assert_bits_equal(at(flat, np.arange(o, o + numels[t])),
+                            synth.normal_bf16(42, st[t], numels[t], 1e-2), f"pack tensor {t}")
+    pad = np.array([b.flat_offset + b.used + j for b in opl.buckets
+                    for j in range(min(16, b.padded - b.used))], dtype=np.int64)
+    if pad.size:
+        assert np.all(at(flat, pad) == 0), "padding not +0"
+    out = torch.full((big,), 0x1111, dtype=torch.int16, device=dev)
+    out2 = torch.full((3,), 0x1111, dtype=torch.int16, device=dev)  # shares the bucket
+    sbp.unpack_params(pl, flat, [None, out, out2], bucket=opl.tensor_bucket[1])
+    H.assert_bits_equal(at(out, idx), want, "unpack of the big tensor")
+    H.assert_bits_equal(H.to_np_u16(out2), synth.normal_bf16(42, st[2], 3, 1e-2), "unpack tensor 2")
+    for s in range(2):  # rank s's chunk of the big tensor's bucket
+        shard = torch.empty(pl.shard_numel, dtype=torch.int16, device=dev)
+        sbp.shard_of(pl, s, flat, shard)
+        b = opl.buckets[opl.tensor_bucket[1]]
+        j = np.unique(np.r_[0, b.chunk - 1, rng.integers(0, b.chunk, 4096)]).astype(np.int64)
+        H.assert_bits_equal(at(shard, b.shard_offset + j), at(flat, b.flat_offset + s * b.chunk + j),
+                            f"shard_of rank {s}")
+    torch.cuda.synchronize()
 
 
 # ---- global gradient-norm clipping ---------------------------------------------
