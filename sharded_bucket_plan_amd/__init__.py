@@ -152,6 +152,24 @@ class Plan:
     def __init__(self, handle, numels):
         self._h = ctypes.c_void_p(handle)
         self.numels = [int(x) for x in numels]
+        self._sizes = None  # (num_tensors, flat_numel, shard_numel), read once
+        self._members = {}  # bucket -> tensor ids with an element in it
+
+    def _cached_sizes(self):
+        if self._sizes is None:
+            L = lib()
+            self._sizes = (L.sbp_plan_num_tensors(self._h), L.sbp_plan_flat_numel(self._h),
+                           L.sbp_plan_shard_numel(self._h))
+        return self._sizes
+
+    def _tensors_of(self, bucket):
+        """Tensor ids a call on `bucket` reads (every tensor for bucket -1)."""
+        if bucket < 0:
+            return range(len(self.numels))
+        ids = self._members.get(bucket)
+        if ids is None:
+            ids = self._members[bucket] = self.bucket_tensors(bucket)
+        return ids
 
     def __del__(self):
         if getattr(self, "_h", None) and _lib is not None and self._h.value:
@@ -288,19 +306,22 @@ def pack_grads(plan, grads, flat, bucket=-1, stream=None):
     grads: one 2-byte device tensor per plan tensor (None allowed for tensors
     outside the selected bucket); flat: 2-byte device tensor of plan.flat_numel.
     """
-    if len(grads) != plan.num_tensors:
+    T, F, _ = plan._cached_sizes()
+    if len(grads) != T:
         raise ValueError("pack_grads: one gradient per plan tensor")
-    if flat.numel() != plan.flat_numel:
+    if flat.numel() != F:
         raise ValueError("pack_grads: flat has the wrong size")
-    arr = (ctypes.c_void_p * max(len(grads), 1))()
-    for t, g in enumerate(grads):
+    if bucket >= plan.num_buckets:
+        raise SbpError(SBP_EINVAL, "pack_grads: bucket out of range")
+    arr = (ctypes.c_void_p * max(T, 1))()
+    for t in plan._tensors_of(int(bucket)):  # only the tensors the call reads
+        g = grads[t]
         if g is None:
             continue
         if g.numel() != plan.numels[t]:
             raise ValueError(f"pack_grads: tensor {t} has {g.numel()} elements")
-        arr[t] = g.data_ptr() if g.numel() else None
         if g.numel():
-            _dev(g, 2, "pack_grads grads")
+            arr[t] = _dev(g, 2, "pack_grads grads")
     _check(lib().sbp_pack_grads(plan.handle, int(bucket), arr, _dev(flat, 2, "pack_grads flat"),
                                 _stream(stream, flat)))
 
@@ -459,12 +480,16 @@ def unpack_params(plan, flat, params, bucket=-1, stream=None):
 
     params: one 2-byte device tensor per plan tensor (None allowed outside the
     selected bucket)."""
-    if len(params) != plan.num_tensors:
+    T, F, _ = plan._cached_sizes()
+    if len(params) != T:
         raise ValueError("unpack_params: one parameter per plan tensor")
-    if flat.numel() != plan.flat_numel:
+    if flat.numel() != F:
         raise ValueError("unpack_params: flat has the wrong size")
-    arr = (ctypes.c_void_p * max(len(params), 1))()
-    for t, p in enumerate(params):
+    if bucket >= plan.num_buckets:
+        raise SbpError(SBP_EINVAL, "unpack_params: bucket out of range")
+    arr = (ctypes.c_void_p * max(T, 1))()
+    for t in plan._tensors_of(int(bucket)):  # only the tensors the call reads
+        p = params[t]
         if p is None:
             continue
         if p.numel() != plan.numels[t]:
