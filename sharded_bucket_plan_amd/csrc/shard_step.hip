@@ -58,6 +58,13 @@
 #ifndef SBP_INFLIGHT_KB
 #define SBP_INFLIGHT_KB 56
 #endif
+// The squared-norm pass ends every block with a block-wide reduction (a
+// barrier); with one block per CU the CU idles through it, so that pass aims
+// at more loads in flight: two blocks per CU at R = 8 with an accumulator
+// (measured 65% -> 71% of 8 TB/s, 80% without the G write).
+#ifndef SBP_NORM_INFLIGHT_KB
+#define SBP_NORM_INFLIGHT_KB 80
+#endif
 #ifndef SBP_XCD_CHUNK
 #define SBP_XCD_CHUNK 64
 #endif
@@ -514,14 +521,15 @@ int64_t tiles_for(int64_t n) {
   return tiles < 1 ? 1 : tiles;
 }
 
-// One block per 2048-element tile; `lane_bytes` = bytes one lane loads.
-Launch launch_for(int64_t n, int lane_bytes) {
+// One block per 2048-element tile; `lane_bytes` = bytes one lane loads;
+// blocks per CU capped to keep about `inflight_kb` KiB of loads in flight.
+Launch launch_for(int64_t n, int lane_bytes, int inflight_kb) {
   Launch L{static_cast<unsigned>(tiles_for(n)), 0};
   const DeviceInfo d = device_info();
-  if (SBP_INFLIGHT_KB > 0 && d.lds_per_cu > 0) {
+  if (inflight_kb > 0 && d.lds_per_cu > 0) {
     const int64_t per_block = static_cast<int64_t>(lane_bytes) * kBlock;
     int64_t blocks_per_cu =
-        (static_cast<int64_t>(SBP_INFLIGHT_KB) * 1024 + per_block / 2) / per_block;
+        (static_cast<int64_t>(inflight_kb) * 1024 + per_block / 2) / per_block;
     if (blocks_per_cu < 1) blocks_per_cu = 1;
     if (blocks_per_cu < 8)  // beyond that the cap no longer binds
       // 512 bytes of slack so exactly blocks_per_cu reservations fit a CU,
@@ -625,15 +633,22 @@ Scalars adamw_scalars(const sbp_adamw_hparams& hp, double bc1, double bc2, float
   return s;
 }
 
-// Launches kernel K with the tile grid and occupancy cap for `lane_bytes`.
+// Launches kernel K with the tile grid and the occupancy cap for
+// `lane_bytes` and `inflight_kb`.
 template <typename K, typename... Args>
-sbp_status launch(const char* who, K kernel, int64_t n, int lane_bytes, hipStream_t stream,
-                  Args... args) {
-  const Launch L = launch_for(n, lane_bytes);
+sbp_status launch_capped(const char* who, K kernel, int64_t n, int lane_bytes, int inflight_kb,
+                         hipStream_t stream, Args... args) {
+  const Launch L = launch_for(n, lane_bytes, inflight_kb);
   sbp_status st = allow_lds(kernel, L.lds);
   if (st != SBP_OK) return st;
   hipLaunchKernelGGL(kernel, dim3(L.grid), dim3(kBlock), L.lds, stream, args...);
   return launched(who);
+}
+
+template <typename K, typename... Args>
+sbp_status launch(const char* who, K kernel, int64_t n, int lane_bytes, hipStream_t stream,
+                  Args... args) {
+  return launch_capped(who, kernel, n, lane_bytes, SBP_INFLIGHT_KB, stream, args...);
 }
 
 }  // namespace
@@ -902,27 +917,20 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
       if (sbp::overlaps(ptr[a], len[a], ptr[b], len[b]))
         return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: buffers overlap");
   const int lane_bytes = 16 * R + (acc ? 32 : 0);
+  constexpr int kNormInflight = SBP_NORM_INFLIGHT_KB;
   st = dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
     const bool wr = g_sum_out != nullptr;
+    auto go = [&](auto kernel) {
+      return launch_capped(who, kernel, n, lane_bytes, kNormInflight, stream, P, acc, scale,
+                           g_sum_out, n, workspace);
+    };
     if constexpr (RR == 0) {
-      if (wr)
-        return launch(who, sq_norm_kernel<0, true, true>, n, lane_bytes, stream, P, acc, scale,
-                      g_sum_out, n, workspace);
-      return launch(who, sq_norm_kernel<0, true, false>, n, lane_bytes, stream, P, acc, scale,
-                    g_sum_out, n, workspace);
+      return wr ? go(sq_norm_kernel<0, true, true>) : go(sq_norm_kernel<0, true, false>);
     } else if (acc) {
-      if (wr)
-        return launch(who, sq_norm_kernel<RR, true, true>, n, lane_bytes, stream, P, acc, scale,
-                      g_sum_out, n, workspace);
-      return launch(who, sq_norm_kernel<RR, true, false>, n, lane_bytes, stream, P, acc, scale,
-                    g_sum_out, n, workspace);
+      return wr ? go(sq_norm_kernel<RR, true, true>) : go(sq_norm_kernel<RR, true, false>);
     } else {
-      if (wr)
-        return launch(who, sq_norm_kernel<RR, false, true>, n, lane_bytes, stream, P, acc,
-                      scale, g_sum_out, n, workspace);
-      return launch(who, sq_norm_kernel<RR, false, false>, n, lane_bytes, stream, P, acc, scale,
-                    g_sum_out, n, workspace);
+      return wr ? go(sq_norm_kernel<RR, false, true>) : go(sq_norm_kernel<RR, false, false>);
     }
   });
   if (st != SBP_OK) return st;
