@@ -136,3 +136,26 @@ def guarded_from(a):
 def canaries_intact(whole, g, fill=0x5A):
     w = whole.cpu().numpy()
     return bool(np.all(w[:g] == fill) and np.all(w[-g:] == fill))
+
+
+def build_c_client(out_dir):
+    """Compile tests/native/abi_c.c, a plain C99 client of include/sbp.h, with
+    gcc and link it against the in-tree libsbp.so; returns the executable."""
+    import os
+    import shutil
+    import subprocess
+
+    import sharded_bucket_plan_amd as sbp
+    if shutil.which("gcc") is None:
+        pytest.skip("needs gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(os.path.abspath(sbp.LIB_PATH))
+    exe = os.path.join(str(out_dir), "abi_c")
+    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+           os.path.join(root, "tests", "native", "abi_c.c"), "-o", exe,
+           "-L", libdir, "-lsbp", "-Wl,-rpath," + libdir,
+           "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return exe

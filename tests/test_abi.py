@@ -393,3 +393,30 @@ def test_grouped_step_validates_before_launch():
     assert call(m=V(0x300000 + 1024)) == sbp.SBP_EINVAL
     assert call(n=0) == sbp.SBP_OK
     assert call(n=0, rs=None, rg=None) == sbp.SBP_OK
+
+
+@pytest.mark.parametrize("name,flags", [("tiny_mlp", 0), ("gpt2_small", 0), ("gpt2_small", 1),
+                                        ("gpt2_small", 2)])
+def test_c_client_plan_matches_oracle(tmp_path, name, flags):
+    """A C99 program using only include/sbp.h builds the plan and reads every
+    query back; the answers equal the oracle's planner."""
+    import subprocess
+    from tests import helpers as H
+    exe = H.build_c_client(tmp_path)
+    w = synth.WORKLOADS[name]
+    cap = w.bucket_cap_bytes if flags != 2 else 1 << 20
+    r = subprocess.run([exe, "plan", str(cap), str(w.world_n), "8", str(flags)]
+                       + [str(x) for x in w.numels], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.split("\n")
+    assert lines[0] == sbp.version()
+    order = "forward" if flags & 1 else "reverse"
+    o = OP.bucket_plan(w.numels, cap, w.world_n, 8, order, split=bool(flags & 2))
+    want = [f"plan {len(w.numels)} {len(o.buckets)} {w.world_n} {o.shard_numel} {o.flat_numel}"]
+    want += [f"tensor {t} {o.tensor_bucket[t]} {o.tensor_offset[t]}" for t in range(len(w.numels))]
+    want += [" ".join(["bucket", str(b), str(ob.used), str(ob.padded), str(ob.chunk),
+                       str(ob.shard_offset), str(ob.flat_offset)] + [str(i) for i in ob.tensors])
+             for b, ob in enumerate(o.buckets)]
+    want += [f"state {s} {OP.state_bytes(o.flat_numel, o.shard_numel, s)}" for s in range(4)]
+    want += ["einval message", ""]
+    assert lines[1:] == want

@@ -708,3 +708,75 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         for a, b, name in zip(outs(), eager, names):
             assert torch.equal(a, b), f"graph replay differs in {name}"
+
+
+@pytest.mark.parametrize("with_acc", [False, True])
+def test_c_client_fused_step(tmp_path, with_acc):
+    """A C99 program using only include/sbp.h and the HIP runtime's C API
+    (its own hipMalloc'd buffers and stream, no torch) runs one fused step;
+    its outputs equal the oracle's bit for bit."""
+    import struct
+    import subprocess
+    exe = H.build_c_client(tmp_path)
+    n, R, t = 256 * 8 * 3 + 37, 3, 3
+    rng = np.random.default_rng(11)
+    peers = H.host_peers(31, t, 1, R, n, 1e-3)
+    acc = (rng.normal(size=n) * 1e-3).astype(np.float32) if with_acc else None
+    th, _, _ = _state(31, n)
+    m = (rng.normal(size=n) * 1e-3).astype(np.float32)
+    v = np.abs(rng.normal(size=n) * 1e-6).astype(np.float32)
+    scale = np.float32(sbp.mean_scale(R, 2 if with_acc else 1))
+    hdr = struct.pack("<qiif5fq", n, R, int(with_acc), float(scale), HP.lr, HP.beta1, HP.beta2,
+                      HP.eps, HP.weight_decay, t)
+    body = b"".join(np.ascontiguousarray(p, np.uint16).tobytes() for p in peers)
+    if with_acc:
+        body += acc.tobytes()
+    body += th.tobytes() + m.tobytes() + v.tobytes()
+    (tmp_path / "in.bin").write_bytes(hdr + body)
+    print(f"c client step n={n} R={R} acc={with_acc}", flush=True)
+    r = subprocess.run([exe, "step", str(tmp_path / "in.bin"), str(tmp_path / "out.bin")],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    out = (tmp_path / "out.bin").read_bytes()
+    assert len(out) == 14 * n
+    got = (np.frombuffer(out, np.float32, n, 0), np.frombuffer(out, np.float32, n, 4 * n),
+           np.frombuffer(out, np.float32, n, 8 * n), np.frombuffer(out, np.uint16, n, 12 * n))
+    want = OS.shard_step(peers, acc, scale, th, m, v, HP, t)
+    worst = H.assert_state_close(got, want, f"C client acc={with_acc}")
+    assert worst == 0, f"expected bit-exact, worst {worst} ulp"
+
+
+def test_bf16_emit_structured_sweep():
+    """The fused kernel's bf16 emit over every upper half-word of an fp32
+    pattern (all signs, exponents and high mantissas, NaN and inf included)
+    times 23 lower half-words (the rounding boundaries 0x7FFF / 0x8000 /
+    0x8001, the extremes and 16 random ones).  With lr = 0 and zero gradients
+    the update leaves every master value unchanged (decay = 1, step = 0), so
+    the emitted parameter is the cast of the input pattern; it equals the
+    oracle's cast bit for bit, NaN by class."""
+    import torch
+    highs = np.arange(65536, dtype=np.uint32) << 16
+    rng = np.random.default_rng(17)
+    lows = np.concatenate([np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF], np.uint32),
+                           rng.integers(0, 65536, 16, dtype=np.uint32)])
+    th = (highs[:, None] | lows[None, :]).reshape(-1).view(np.float32)
+    n = th.size
+    hp = sbp.AdamW(0.0, 0.9, 0.999, 1e-8, 0.01)
+    zero = np.zeros(n, np.uint16)
+    dz = H.from_np_u16(zero)
+    dth, dm, dv = H.from_np_f32(th), H.from_np_f32(np.zeros(n, np.float32)), \
+        H.from_np_f32(np.zeros(n, np.float32))
+    dp = H.empty_u16(n)
+    sbp.adamw_shard([dz], None, 1.0, dth, dm, dv, dp, hp, 1)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        want = OS.shard_step([zero], None, np.float32(1.0), th, np.zeros(n, np.float32),
+                             np.zeros(n, np.float32), hp, 1)
+    got_th, got_p = H.to_np_f32(dth), H.to_np_u16(dp)
+    nan = np.isnan(th)
+    assert np.array_equal(np.isnan(want[0]), nan) and np.array_equal(np.isnan(got_th), nan)
+    H.assert_bits_equal(got_th[~nan], th[~nan], "master passes through")
+    H.assert_bits_equal(got_p[~nan], want[3][~nan], "bf16 emit")
+    H.assert_bits_equal(want[3][~nan], OS.f32_to_bf16(th[~nan]), "oracle emit is the cast")
+    pn = got_p[nan].astype(np.uint32) << 16
+    assert np.all(np.isnan(pn.view(np.float32))), "NaN emits a NaN"
