@@ -22,7 +22,8 @@ Variants of the step (same JSON line): --clip MAX_NORM adds global-norm
 clipping (the norm pass writing G, then the update from G); --groups uses
 two parameter groups (no weight decay on 1-D tensors) and the grouped step.
 Other modes print their own JSON: --layout times pack / shard_of /
-gather_shards / unpack_params and the plan builds on the workload's model; --bucket-sweep times one
+gather_shards / unpack_params and the plan builds on the workload's model
+(--plan whole | split | per_tensor picks the layout); --bucket-sweep times one
 accumulate pass per bucket for caps of 1..256 MiB on the 7.5B shard;
 --calibrate-copy and --summarize-pmc make the HBM-counter summary.
 
@@ -461,9 +462,12 @@ def bucket_sweep(seed, reps=5):
     return {"bucket_sweep": rows, "fit": fit, "bytes_per_pass": M, "shard_numel": n}
 
 
-def layout_moves(seed, workload="llama3_8b", reps=5):
+def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     """The layout calls on a workload's model (default Llama-3-8B at N = 8:
-    162 buckets of 291 tensors, 8,030,261,248 elements): rank 0's chunks of one rank's flat buckets
+    162 buckets of 291 tensors, 8,030,261,248 elements) under one plan kind
+    (whole: tensors whole in capped buckets; split: fixed-size buckets with
+    tensors split across them; per_tensor: one bucket per tensor, dim-0 row
+    shards): rank 0's chunks of one rank's flat buckets
     (shard_of: what that rank contributes to owner 0 in the reduce-scatter),
     the 8 shards into the flat buckets (gather_shards: the all-gather's
     layout), and the flat buckets into the 291 per-tensor parameters
@@ -480,7 +484,13 @@ def layout_moves(seed, workload="llama3_8b", reps=5):
 
     w = synth.WORKLOADS[workload]
     dev = torch.device("cuda:0")
-    pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
+    if plan_kind == "split":
+        pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n, split=True)
+    elif plan_kind == "per_tensor":
+        pl = sbp.bucket_plan_per_tensor(w.numels, w.world_n, rows)
+    else:
+        pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n, F, P = pl.shard_numel, pl.flat_numel, sum(w.numels)
     flat = torch.empty(F, dtype=torch.int16, device=dev)
     shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
@@ -535,7 +545,6 @@ def layout_moves(seed, workload="llama3_8b", reps=5):
             f"{call:.3f} ms per Python call")
     # the plans themselves (host only, made once per model): microseconds per build
     plans = {}
-    rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
     for name, make in (("bucket_plan", lambda: sbp.bucket_plan(w.numels, w.bucket_cap_bytes,
                                                                 w.world_n)),
                        ("bucket_plan split", lambda: sbp.bucket_plan(w.numels, w.bucket_cap_bytes,
@@ -548,7 +557,8 @@ def layout_moves(seed, workload="llama3_8b", reps=5):
             make()
         plans[name] = {"us_per_plan": (time.perf_counter() - t0) / 200 * 1e6}
         log(f"layout: {name} {plans[name]['us_per_plan']:.1f} us per plan")
-    return {"layout_moves": out, "plans": plans, "workload": workload, "N": w.world_n,
+    return {"layout_moves": out, "plans": plans, "workload": workload, "plan": plan_kind,
+            "N": w.world_n,
             "shard_numel": n, "flat_numel": F, "tensors": len(w.numels),
             "buckets": pl.num_buckets}
 
@@ -573,6 +583,9 @@ def main():
     ap.add_argument("--layout", action="store_true",
                     help="only time the layout calls (pack, shard_of, gather, unpack) and the "
                          "plan builds on --workload's model and print their JSON")
+    ap.add_argument("--plan", choices=["whole", "split", "per_tensor"], default="whole",
+                    help="with --layout: the plan whose layout is timed (whole-tensor buckets, "
+                         "fixed-size split buckets, or one bucket per tensor with row shards)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5,
@@ -600,7 +613,7 @@ def main():
         print(json.dumps(bucket_sweep(seed)), flush=True)
         return
     if args.layout:
-        print(json.dumps(layout_moves(seed, args.workload)), flush=True)
+        print(json.dumps(layout_moves(seed, args.workload, args.plan)), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),

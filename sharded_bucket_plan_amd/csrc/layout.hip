@@ -49,12 +49,15 @@ constexpr int kRounds = SBP_PACK_ROUNDS;
 constexpr int kXcds = 8;
 constexpr int64_t kChunk = static_cast<int64_t>(kBlock) * 8 * kRounds;  // elements
 constexpr int kMaxSegs = 160;
-// A list that does not fit one launch goes out in launches of at most this
-// many segments: a shorter list per launch keeps each block's segment search
-// shallow (measured: Llama-3-8B pack 79.2% of 8 TB/s with 64 per launch, 78.0%
-// with 160), while a list that fits one launch saves the second launch
-// (GPT-2-small pack: 70.3% in one launch against 65.8% in two).
+// A list that does not fit one launch goes out in several.  A launch is cut
+// at this many segments once it holds kBigLaunchChunks chunks: a shorter list
+// per launch keeps each block's segment search shallow (measured: Llama-3-8B
+// pack 79.2% of 8 TB/s with 64 per launch, 78.0% with 160).  A launch of
+// small segments is filled up to kMaxSegs instead, since each launch's ramp
+// and drain cost a few microseconds; likewise a list that fits one launch
+// goes out in one (GPT-2-small pack: 70.3% in one launch against 65.8% in two).
 constexpr int kSegsPerLaunchWhenSplit = 64;
+constexpr int32_t kBigLaunchChunks = 1 << 15;  // 64M elements, ~40 us of copying
 constexpr int64_t kMaxPiece = int64_t{1} << 30;  // longer segments are split (a multiple of kChunk)
 
 // A copy segment as the kernel sees it: 24 bytes, so 160 fit in the kernel
@@ -131,12 +134,14 @@ sbp_status launch_segments(const char* who, const std::vector<Seg>& segs, hipStr
   };
   int64_t pieces = 0;
   for (const Seg& s : segs) pieces += (s.len + kMaxPiece - 1) / kMaxPiece;
-  const int per_launch = pieces <= kMaxSegs ? kMaxSegs : kSegsPerLaunchWhenSplit;
+  const bool one_launch = pieces <= kMaxSegs;
   for (const Seg& s : segs) {
     for (int64_t off = 0; off < s.len; off += kMaxPiece) {
       const int64_t len = std::min(kMaxPiece, s.len - off);
       const int64_t ch = (len + kChunk - 1) / kChunk;
-      if (L.count == per_launch || L.chunks + ch > INT32_MAX) {
+      const bool cut_early =
+          !one_launch && L.count >= kSegsPerLaunchWhenSplit && L.chunks >= kBigLaunchChunks;
+      if (L.count == kMaxSegs || cut_early || L.chunks + ch > INT32_MAX) {
         sbp_status st = flush();
         if (st != SBP_OK) return st;
       }
