@@ -22,7 +22,7 @@ Variants of the step (same JSON line): --clip MAX_NORM adds global-norm
 clipping (the norm pass writing G, then the update from G); --groups uses
 two parameter groups (no weight decay on 1-D tensors) and the grouped step.
 Other modes print their own JSON: --layout times pack / shard_of /
-gather_shards / unpack_params and the plan builds on the workload's model
+gather_shards / unpack_params / unpack_shards and the plan builds on the workload's model
 (--plan whole | split | per_tensor picks the layout); --bucket-sweep times one
 accumulate pass per bucket for caps of 1..256 MiB on the 7.5B shard;
 --calibrate-copy and --summarize-pmc make the HBM-counter summary.
@@ -471,8 +471,9 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     (shard_of: what that rank contributes to owner 0 in the reduce-scatter),
     the 8 shards into the flat buckets (gather_shards: the all-gather's
     layout), and the flat buckets into the 291 per-tensor parameters
-    (unpack_params), as well as pack_grads (per-tensor gradients into the
-    buckets).  Each call is timed with events on the launch stream, median of
+    (unpack_params), the 8 shards straight into the per-tensor parameters
+    (unpack_shards: gather and unpack in one pass), as well as pack_grads
+    (per-tensor gradients into the buckets).  Each call is timed with events on the launch stream, median of
     `reps`, twice: as a Python call (host marshalling included) and as a
     replay of a graph holding the call's launches k times (GPU time, which
     the roofline figures use; k spreads the graph's own launch cost); algorithmic bytes are one read and one write per element
@@ -504,6 +505,7 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
         "shard_of": (lambda: sbp.shard_of(pl, 0, flat, shards[0]), 4 * n),
         "gather_shards": (lambda: sbp.gather_shards(pl, shards, flat), 4 * F),
         "unpack_params": (lambda: sbp.unpack_params(pl, flat, tensors), 4 * P),
+        "unpack_shards": (lambda: sbp.unpack_shards(pl, shards, tensors), 4 * P),
     }
     def timed(run):
         ms = []

@@ -230,6 +230,15 @@ sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
  *   ...] for every selected bucket: the layout an all-gather of the bf16
  *   parameter shards produces.  shards: host array of N device pointers
  *   (16-B aligned, shard_numel elements each), disjoint from flat.
+ * sbp_unpack_shards: the N ranks' shards -> per-tensor bf16 parameters in
+ *   one pass: the same result as sbp_gather_shards into a flat buffer
+ *   followed by sbp_unpack_params, without the flat buffer and its extra
+ *   write and read ("Parallelisms", ZeRO-3: a layer's parameter shards are
+ *   all-gathered just before it runs; YaFSDP: fewer memory operations
+ *   around the collectives).  Each tensor element inside the selected
+ *   bucket(s) is read from the shard of the rank that owns it; padding is
+ *   not read.  shards as for sbp_gather_shards; tensor_params as for
+ *   sbp_unpack_params, disjoint from each other and from every shard.
  * Errors: SBP_EINVAL (null, rank or bucket out of range, overlap),
  * SBP_EALIGN, SBP_ERANGE, SBP_EHIP.
  * ---------------------------------------------------------------------- */
@@ -241,6 +250,9 @@ sbp_status sbp_shard_of(const sbp_plan* plan, int32_t bucket, int32_t rank,
 sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket,
                              const void* const* shards, void* flat,
                              hipStream_t stream);
+sbp_status sbp_unpack_shards(const sbp_plan* plan, int32_t bucket,
+                             const void* const* shards,
+                             void* const* tensor_params, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Reduce ("Parallelisms", ZeRO-1: reduce-scatter leaves each worker the

@@ -9,7 +9,7 @@ call fails, an error is raised.
 Functions (same names as the C calls without the "sbp_" prefix):
   plans        bucket_plan (whole-tensor or split buckets), bucket_plan_per_tensor
                (one bucket per tensor, dim-0 row shards), Plan queries
-  layout       pack_grads, unpack_params, shard_of, gather_shards
+  layout       pack_grads, unpack_params, shard_of, gather_shards, unpack_shards
   scales       mean_scale, tokens_scale, clip_scale
   shard step   reduce_shard, accumulate_grads, adamw_shard, grad_sq_norm
                (+ grad_sq_norm_workspace)
@@ -37,7 +37,7 @@ EXPORTS = (
     "sbp_pack_grads", "sbp_reduce_shard", "sbp_accumulate_grads", "sbp_adamw_shard",
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
     "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards", "sbp_bucket_plan_per_tensor",
-    "sbp_group_runs", "sbp_adamw_shard_grouped",
+    "sbp_group_runs", "sbp_adamw_shard_grouped", "sbp_unpack_shards",
 )
 
 MAX_GROUPS = 8
@@ -117,6 +117,7 @@ def lib():
                           ctypes.c_void_p, ctypes.c_void_p], st),
         "sbp_gather_shards": ([ctypes.c_void_p, ctypes.c_int32, _vpp, ctypes.c_void_p,
                                ctypes.c_void_p], st),
+        "sbp_unpack_shards": ([ctypes.c_void_p, ctypes.c_int32, _vpp, _vpp, ctypes.c_void_p], st),
         "sbp_group_runs": ([ctypes.c_void_p, ctypes.c_int32, _i32p, _i64p, _i32p,
                             ctypes.c_int64, _i64p], st),
         "sbp_adamw_shard_grouped": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
@@ -516,3 +517,31 @@ def gather_shards(plan, shards, flat, bucket=-1, stream=None):
         raise ValueError("gather_shards: flat or a shard has the wrong size")
     _check(lib().sbp_gather_shards(plan.handle, int(bucket), _ptrs(shards, "gather_shards shards"),
                                    _dev(flat, 2, "gather_shards flat"), _stream(stream, flat)))
+
+
+def unpack_shards(plan, shards, params, bucket=-1, stream=None):
+    """sbp_unpack_shards: the N ranks' shards -> per-tensor bf16 parameters in
+    one pass (gather_shards followed by unpack_params, without the flat buffer).
+
+    params: one 2-byte device tensor per plan tensor (None allowed outside the
+    selected bucket)."""
+    T, _, _ = plan._cached_sizes()
+    if len(shards) != plan.world_n:
+        raise ValueError("unpack_shards: one shard per rank")
+    if any(x.numel() != plan.shard_numel for x in shards):
+        raise ValueError("unpack_shards: a shard has the wrong size")
+    if len(params) != T:
+        raise ValueError("unpack_shards: one parameter per plan tensor")
+    if bucket >= plan.num_buckets:
+        raise SbpError(SBP_EINVAL, "unpack_shards: bucket out of range")
+    arr = (ctypes.c_void_p * max(T, 1))()
+    for t in plan._tensors_of(int(bucket)):  # only the tensors the call writes
+        p = params[t]
+        if p is None:
+            continue
+        if p.numel() != plan.numels[t]:
+            raise ValueError(f"unpack_shards: tensor {t} has {p.numel()} elements")
+        if p.numel():
+            arr[t] = _dev(p, 2, "unpack_shards params")
+    _check(lib().sbp_unpack_shards(plan.handle, int(bucket), _ptrs(shards, "unpack_shards shards"),
+                                   arr, _stream(stream, shards[0])))

@@ -28,5 +28,7 @@ sbp_status shard_of_segments(const sbp_plan* plan, int32_t bucket, int32_t rank,
                              void* shard, std::vector<Seg>& segs);
 sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
                            void* flat, std::vector<Seg>& segs);
+sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                                  void* const* tensor_params, std::vector<Seg>& segs);
 
 }  // namespace sbp

@@ -186,4 +186,11 @@ sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket, const void* c
   return st != SBP_OK ? st : launch_segments("sbp_gather_shards", segs, stream);
 }
 
+sbp_status sbp_unpack_shards(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                             void* const* tensor_params, hipStream_t stream) {
+  std::vector<Seg> segs;
+  sbp_status st = sbp::unpack_shards_segments(plan, bucket, shards, tensor_params, segs);
+  return st != SBP_OK ? st : launch_segments("sbp_unpack_shards", segs, stream);
+}
+
 }  // extern "C"

@@ -219,6 +219,63 @@ sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* con
   return sbp::ok();
 }
 
+// Each tensor piece of a selected bucket is cut where the bucket's rank
+// chunks meet; each cut part is read from the shard of the rank that owns it.
+sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                                  void* const* tensor_params, std::vector<Seg>& out) {
+  out.clear();
+  const char* who = "sbp_unpack_shards";
+  if (plan == nullptr || shards == nullptr || tensor_params == nullptr)
+    return sbp::fail(SBP_EINVAL, "sbp_unpack_shards: null argument");
+  for (int32_t s = 0; s < plan->world_n; ++s) {
+    if (shards[s] == nullptr) return sbp::fail(SBP_EINVAL, "sbp_unpack_shards: a shard is null");
+    if (!sbp::aligned(shards[s], 16))
+      return sbp::fail(SBP_EALIGN, "sbp_unpack_shards: shards must be 16-byte aligned");
+  }
+  int32_t b0, b1;
+  int64_t lo, hi;
+  sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
+  if (st != SBP_OK) return st;
+  std::vector<Seg> segs;
+  try {
+    std::vector<std::pair<uintptr_t, int64_t>> outs;
+    std::vector<char> seen(plan->numel.size(), 0);
+    for (int32_t b = b0; b < b1; ++b) {
+      const sbp::Bucket& k = plan->buckets[b];
+      if (k.chunk == 0) continue;
+      for (const Piece& pc : pieces_in(plan, k.flat_offset, k.flat_offset + k.padded)) {
+        void* dst = tensor_params[pc.t];
+        if (dst == nullptr)
+          return sbp::fail(SBP_EINVAL, "sbp_unpack_shards: parameter pointer of a tensor is null");
+        if (!sbp::aligned(dst, 2))
+          return sbp::fail(SBP_EALIGN, "sbp_unpack_shards: parameters must be 2-byte aligned");
+        if (!seen[pc.t]) {
+          const int64_t bytes = 2 * plan->numel[pc.t];
+          for (int32_t s = 0; s < plan->world_n; ++s)
+            if (sbp::overlaps(dst, bytes, shards[s], 2 * plan->shard_numel))
+              return sbp::fail(SBP_EINVAL, "sbp_unpack_shards: a parameter overlaps a shard");
+          outs.push_back({reinterpret_cast<uintptr_t>(dst), bytes});
+          seen[pc.t] = 1;
+        }
+        const int64_t rel = pc.flat - k.flat_offset;  // piece start inside the bucket
+        for (int64_t s = rel / k.chunk; s * k.chunk < rel + pc.len; ++s) {
+          const int64_t a = std::max(rel, s * k.chunk);
+          const int64_t e = std::min(rel + pc.len, (s + 1) * k.chunk);
+          segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + k.shard_offset +
+                                 (a - s * k.chunk),
+                             static_cast<uint16_t*>(dst) + pc.elem + (a - rel), e - a});
+        }
+      }
+    }
+    if (!disjoint(outs))
+      return sbp::fail(SBP_EINVAL, "sbp_unpack_shards: parameter buffers overlap");
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, "sbp_unpack_shards: out of host memory");
+  }
+  out.swap(segs);
+  return sbp::ok();
+}
+
 }  // namespace sbp
 
 using sbp::Piece;

@@ -1,5 +1,5 @@
 // Host fuzz driver for the copy-segment builders of the layout calls (pack,
-// unpack, shard_of, gather), built with AddressSanitizer and
+// unpack, shard_of, gather, unpack_shards), built with AddressSanitizer and
 // UndefinedBehaviorSanitizer by tests/test_native_sanitize.py.  The GPU copy
 // kernel executes these segment lists as they are, so a segment outside its
 // buffers would be an out-of-bounds device write.  Here every list is
@@ -201,6 +201,35 @@ void one_case(const Case& c) {
         CHECK(shards[s].p[so + j] == (sel ? flat.p[fo + s * chunk + j] : kSentinel));
   }
 
+  // unpack_shards: what gather followed by unpack gives, in one list, from
+  // shards whose every slot (padding included) holds data
+  for (int32_t s = 0; s < c.N; ++s)
+    for (int64_t j = 0; j < S; ++j) shards[s].p[j] = static_cast<uint16_t>(s * 7919 + j * 13 + 3);
+  if (T > 0) {
+    Buf ref(F);
+    CHECK(sbp::gather_segments(p, bucket, shard_ptrs.data(), ref.p, segs) == SBP_OK);
+    run(segs, {&ref}, shard_bufs, written);
+    std::vector<Buf> outs;
+    std::vector<void*> out_ptrs(T);
+    std::vector<Buf*> out_bufs;
+    for (int32_t t = 0; t < T; ++t) outs.emplace_back(c.numel[t]);
+    for (int32_t t = 0; t < T; ++t) {
+      out_ptrs[t] = outs[t].p;
+      out_bufs.push_back(&outs[t]);
+    }
+    CHECK(sbp::unpack_shards_segments(p, bucket, shard_ptrs.data(), out_ptrs.data(), segs) ==
+          SBP_OK);
+    run(segs, out_bufs, shard_bufs, written);
+    for (int32_t t = 0; t < T; ++t) {
+      const int64_t a = tensor_flat(p, t);
+      for (int64_t i = 0; i < c.numel[t]; ++i) {
+        const bool sel = a + i >= lo && a + i < hi;
+        CHECK(written[t][i] == (sel ? 1 : 0));
+        CHECK(outs[t].p[i] == (sel ? ref.p[a + i] : kSentinel));
+      }
+    }
+  }
+
   // run tables: the groups over each shard start at 0, ascend, and fit
   std::vector<int32_t> tg(T > 0 ? T : 1);
   for (int32_t t = 0; t < T; ++t) tg[t] = static_cast<int32_t>(rng() % SBP_MAX_GROUPS);
@@ -249,6 +278,16 @@ int main(int argc, char** argv) {
     CHECK(sbp::pack_segments(p, -1, srcs, buf, segs) == SBP_EINVAL && segs.empty());
     segs.resize(2);
     CHECK(sbp::shard_of_segments(p, 5, 0, buf, buf + 128, segs) == SBP_EINVAL && segs.empty());
+    // tensor 1's segments are listed before tensor 0's null parameter is found
+    const void* shard_list[1] = {buf};
+    void* params[2] = {nullptr, buf + 128};
+    segs.resize(2);
+    CHECK(sbp::unpack_shards_segments(p, -1, shard_list, params, segs) == SBP_EINVAL &&
+          segs.empty());
+    // a parameter on top of a shard
+    void* clash[2] = {buf + 200, buf + 8};
+    CHECK(sbp::unpack_shards_segments(p, -1, shard_list, clash, segs) == SBP_EINVAL &&
+          segs.empty());
     sbp_plan_free(p);
   }
   printf("layout cases %d ok\n", iters);

@@ -259,6 +259,20 @@ def test_layout_calls_validate_before_launch():
     assert L.sbp_gather_shards(plan.handle, -1, two, V(0x100000), None) == sbp.SBP_EINVAL
     assert L.sbp_gather_shards(plan.handle, -1, (V * 2)(0x100004, 0x200000), V(0x300000),
                                None) == sbp.SBP_EALIGN
+    shards = (V * 2)(0x500000, 0x600000)
+    assert L.sbp_unpack_shards(None, -1, shards, two, None) == sbp.SBP_EINVAL
+    assert L.sbp_unpack_shards(plan.handle, 3, shards, two, None) == sbp.SBP_EINVAL
+    assert L.sbp_unpack_shards(plan.handle, -1, (V * 2)(0x500000, None), two,
+                               None) == sbp.SBP_EINVAL
+    assert L.sbp_unpack_shards(plan.handle, -1, (V * 2)(0x500008, 0x600000), two,
+                               None) == sbp.SBP_EALIGN
+    assert L.sbp_unpack_shards(plan.handle, -1, shards, (V * 2)(0x100001, 0x200000),
+                               None) == sbp.SBP_EALIGN
+    assert L.sbp_unpack_shards(plan.handle, -1, shards, (V * 2)(0x100000, 0x100010),
+                               None) == sbp.SBP_EINVAL  # the two outputs overlap
+    assert L.sbp_unpack_shards(plan.handle, -1, shards, (V * 2)(0x100000, 0x600004),
+                               None) == sbp.SBP_EINVAL  # an output inside a shard
+    assert b"overlaps a shard" in L.sbp_last_error()
 
 
 def test_per_tensor_plan_matches_oracle():

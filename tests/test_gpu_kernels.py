@@ -624,6 +624,25 @@ def test_layout_moves(kind, misalign):
     for t, h in enumerate(grads_h):
         H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack tensor {t}")
         H.assert_bits_equal(H.to_np_u16(outs2[t]), h, f"unpack by bucket, tensor {t}")
+    # shards -> per-tensor parameters in one pass (the oracle's gather, then its
+    # unpack), from shards with nonzero padding slots, which must not be read
+    rnd = [synth.normal_bf16(32, synth.peer_stream(1, 0, s), pl.shard_numel, 1.0)
+           for s in range(N)]
+    dsh = [x[1] for x in shard_g]  # 16-byte aligned, as the call requires
+    for d, x in zip(dsh, rnd):
+        d.copy_(H.from_np_u16(x))
+    want_t = OS.unpack(opl, OS.gather(opl, rnd))
+    outs3 = [dev_tensor(np.zeros(n, np.uint16)) for n in numels]
+    sbp.unpack_shards(pl, dsh, outs3)
+    outs4 = [dev_tensor(np.zeros(n, np.uint16)) for n in numels]
+    for b in range(pl.num_buckets):
+        members = set(pl.bucket_tensors(b))
+        sbp.unpack_shards(pl, dsh, [outs4[t] if t in members else None
+                                    for t in range(len(numels))], bucket=b)
+    torch.cuda.synchronize()
+    for t, h in enumerate(want_t):
+        H.assert_bits_equal(H.to_np_u16(outs3[t]), h, f"unpack_shards tensor {t}")
+        H.assert_bits_equal(H.to_np_u16(outs4[t]), h, f"unpack_shards by bucket, tensor {t}")
     assert guards_ok(), "a write outside a per-tensor buffer"
 
 
@@ -631,7 +650,7 @@ def test_graph_capture_replays():
     """The calls allocate nothing and pass their tables by value, so a step can
     be captured in a HIP graph.  The captured step uses every device entry
     point: pack, shard_of, accumulate, reduce, the squared norm, the fused
-    step from G, the grouped fused step, gather and unpack.  Each replay
+    step from G, the grouped fused step, gather, unpack and unpack_shards.  Each replay
     starts from the same saved state (restored by eager copies between
     replays) and must equal the eager run."""
     import torch
@@ -658,6 +677,7 @@ def test_graph_capture_replays():
     p2 = H.empty_u16(n)
     gathered = H.empty_u16(n)
     params = [H.empty_u16(k) for k in numels]
+    params2 = [H.empty_u16(k) for k in numels]
     ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=H.dev())
     sq = torch.empty(1, dtype=torch.float64, device=H.dev())
     scale = sbp.mean_scale(R, 2)
@@ -674,11 +694,13 @@ def test_graph_capture_replays():
         sbp.adamw_shard_grouped([shard, other], acc, scale, *work2, p2, HP, 1, groups, rs, rg)
         sbp.gather_shards(pl, [p2], gathered)
         sbp.unpack_params(pl, gathered, params)
+        sbp.unpack_shards(pl, [p], params2)
 
-    outs = lambda: work + work2 + [p, p2, sq, red, gathered] + params
+    outs = lambda: work + work2 + [p, p2, sq, red, gathered] + params + params2
     names = (["master", "m", "v", "grouped master", "grouped m", "grouped v", "param",
               "grouped param", "sq", "reduced", "gathered"] +
-             [f"param tensor {t}" for t in range(len(numels))])
+             [f"param tensor {t}" for t in range(len(numels))] +
+             [f"unpack_shards tensor {t}" for t in range(len(numels))])
     step()
     torch.cuda.synchronize()
     eager = [x.clone() for x in outs()]
@@ -686,7 +708,7 @@ def test_graph_capture_replays():
     def reset():
         for x, y in zip(work + work2, init + init):
             x.copy_(y)
-        for x in (p, p2, gathered, *params):
+        for x in (p, p2, gathered, *params, *params2):
             x.fill_(0)
         for x in (sq, red):
             x.fill_(-1.0)
