@@ -287,12 +287,61 @@ def test_llama3_8b_dp_pack_and_step_sampled():
         H.assert_bits_equal(a, b, f"llama3_8b_dp {name}")
 
 
+@pytest.mark.parametrize("kind", ["whole", "per_tensor"])
+def test_llama3_8b_all_gather_side_sampled(kind):
+    """The all-gather side at full Llama-3-8B scale (N = 8, 8.03B parameter
+    elements, flat positions beyond 2^32): the eight bf16 parameter shards go
+    straight into the 291 per-tensor parameters (unpack_shards).  Sampled
+    elements of every tensor (its first, its last and random ones) against the
+    oracle plan's all-gather layout, element by element: element i of tensor t
+    sits at flat position a = offset(t) + i of its bucket, which the gather
+    fills from shard s = (a - bucket start) // chunk at the bucket's shard
+    offset plus (a - bucket start - s * chunk)."""
+    import torch
+    w = synth.WORKLOADS["llama3_8b"]
+    rows = [x[1] if len(x) == 2 else 1 for _, x in w.params]
+    if kind == "per_tensor":
+        pl = sbp.bucket_plan_per_tensor(w.numels, w.world_n, rows)
+        opl = OP.per_tensor_plan(w.numels, w.world_n, rows)
+    else:
+        pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+        opl = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    N, n = w.world_n, pl.shard_numel
+    assert n == opl.shard_numel and pl.flat_numel > 1 << 32
+    shards = []
+    for s in range(N):
+        x = H.empty_u16(n)
+        synth.dev_normal_bf16(x, SEED, synth.peer_stream(1, 0, s), 1.0)
+        shards.append(x)
+    params = [H.empty_u16(k) for k in w.numels]
+    sbp.unpack_shards(pl, shards, params)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    fo_all = np.array([b.flat_offset for b in opl.buckets], np.int64)
+    ch_all = np.array([b.chunk for b in opl.buckets], np.int64)
+    so_all = np.array([b.shard_offset for b in opl.buckets], np.int64)
+    for t, k in enumerate(w.numels):
+        i = np.unique(np.concatenate([[0, k - 1], rng.integers(0, k, 64)])).astype(np.int64)
+        a = opl.tensor_flat_offset(t) + i
+        b = np.searchsorted(fo_all, a, side="right") - 1
+        rel = a - fo_all[b]
+        s = rel // ch_all[b]
+        j = so_all[b] + rel - s * ch_all[b]
+        want = np.empty(i.size, np.uint16)
+        for r in np.unique(s):
+            sel = s == r
+            want[sel] = synth.normal_bf16_at(SEED, synth.peer_stream(1, 0, int(r)), j[sel], 1.0)
+        got = H.to_np_u16(params[t].index_select(0, torch.from_numpy(i).to(H.dev())))
+        H.assert_bits_equal(got, want, f"{kind} plan, tensor {t}")
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_tiny_mlp_zero_round_trip(split):
     """Both ranks of the 2-layer MLP on one GPU, each step: every rank packs its
     per-tensor gradients, each owner takes its chunk of every rank's buckets
     (shard_of), reduces and updates its shard, the bf16 shards are gathered
-    and unpacked into per-tensor parameters -- the reduce-scatter / update /
+    and unpacked into per-tensor parameters (in two calls, and in one with
+    unpack_shards) -- the reduce-scatter / update /
     all-gather round trip, all in the library's kernels, against the oracle."""
     import torch
     w = synth.WORKLOADS["tiny_mlp"]
@@ -313,6 +362,7 @@ def test_tiny_mlp_zero_round_trip(split):
     recv = [[H.empty_u16(n) for _ in range(R)] for _ in range(N)]
     gathered = H.empty_u16(pl.flat_numel)
     params = [H.empty_u16(k) for k in w.numels]
+    params1 = [H.empty_u16(k) for k in w.numels]  # the one-pass all-gather side
     for t in range(1, 4):
         host_flats = []
         for r in range(R):
@@ -334,10 +384,13 @@ def test_tiny_mlp_zero_round_trip(split):
             oshards.append(p)
         sbp.gather_shards(pl, [state[s][3] for s in range(N)], gathered)
         sbp.unpack_params(pl, gathered, params)
+        sbp.unpack_shards(pl, [state[s][3] for s in range(N)], params1)
         torch.cuda.synchronize()
         want = OS.unpack(opl, OS.gather(opl, oshards))
         for tid in range(len(w.numels)):
             H.assert_bits_equal(H.to_np_u16(params[tid]), want[tid], f"step {t} tensor {tid}")
+            H.assert_bits_equal(H.to_np_u16(params1[tid]), want[tid],
+                                f"step {t} tensor {tid}, unpack_shards")
 
 
 def test_shard_union_resume_and_reshard():
