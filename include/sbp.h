@@ -63,6 +63,12 @@ typedef int32_t sbp_status;
 #define SBP_ENOMEM (-5) /* host allocation failed                            */
 
 #define SBP_MAX_PEERS 16 /* largest R accepted by the reduce-type calls */
+/* Largest n of one reduce, accumulate, fused-step or squared-norm call:
+ * one launch covers the whole range with one 256-lane block per 2048
+ * elements, and a launch holds at most 2^32 - 1 work-items, so at most
+ * 2^24 - 1 blocks.  Larger shards are stepped in ranges (the calls are
+ * elementwise; a range's pointers are the shard's plus its offset). */
+#define SBP_MAX_SHARD_NUMEL 34359736320LL /* (2^24 - 1) * 2048 */
 #define SBP_MAX_GROUPS 8 /* parameter groups of the grouped AdamW step    */
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -266,7 +272,8 @@ sbp_status sbp_unpack_shards(const sbp_plan* plan, int32_t bucket,
  * R      1..SBP_MAX_PEERS
  * out    device fp32[n]
  * All device pointers 16-byte aligned; out must not overlap a peer.
- * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL),
+ * SBP_EHIP.
  * ---------------------------------------------------------------------- */
 sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n,
                             float scale, float* out, hipStream_t stream);
@@ -280,7 +287,8 @@ sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n,
  * scaling (the scale is applied once, in the fused step).  R = 1 is a
  * rank's local (no_sync) accumulation; R > 1 accumulates reduce-scattered
  * shards.  acc is read and written in place.
- * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL),
+ * SBP_EHIP.
  * ---------------------------------------------------------------------- */
 sbp_status sbp_accumulate_grads(float* acc, const void* const* peers,
                                 int32_t R, int64_t n, int32_t first,
@@ -318,7 +326,8 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers,
  * hp         hyperparameters; hp->step = t >= 1 (1-based, once per
  *            optimizer step, not per microbatch)
  * All device pointers 16-byte aligned and pairwise non-overlapping.
- * Errors: SBP_EINVAL, SBP_EALIGN, SBP_EHIP.
+ * Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL),
+ * SBP_EHIP.
  * ---------------------------------------------------------------------- */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
@@ -401,7 +410,8 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
  *                             workspace_len >= sbp_grad_sq_norm_workspace(n)
  *   sq_out                    device double, 8-B aligned (n == 0 writes 0)
  *   Outputs must not overlap any other buffer.
- *   Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE, SBP_EHIP.
+ *   Errors: SBP_EINVAL (also a workspace shorter than needed), SBP_EALIGN,
+ *   SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL), SBP_EHIP.
  *
  * sbp_clip_scale (host): with total_sq the sum of all ranks' squared norms,
  *   coef = min(1, max_norm / (sqrt(total_sq) + 1e-6)) in float64 (a NaN norm

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libsbp.so")
 
 SBP_OK, SBP_EINVAL, SBP_EALIGN, SBP_ERANGE, SBP_EHIP, SBP_ENOMEM = 0, -1, -2, -3, -4, -5
 SBP_MAX_PEERS = 16
+MAX_SHARD_NUMEL = (2 ** 24 - 1) * 2048  # SBP_MAX_SHARD_NUMEL: n of one step call
 ORDER_REVERSE, ORDER_FORWARD, SPLIT_TENSORS = 0, 1, 2
 
 # every function include/sbp.h declares

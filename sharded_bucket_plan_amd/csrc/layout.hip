@@ -59,6 +59,8 @@ constexpr int kMaxSegs = 160;
 constexpr int kSegsPerLaunchWhenSplit = 64;
 constexpr int32_t kBigLaunchChunks = 1 << 15;  // 64M elements, ~40 us of copying
 constexpr int64_t kMaxPiece = int64_t{1} << 30;  // longer segments are split (a multiple of kChunk)
+// One block per chunk, and a launch holds at most 2^32 - 1 work-items.
+constexpr int64_t kMaxLaunchChunks = (int64_t{1} << 32) / kBlock - 1;
 
 // A copy segment as the kernel sees it: 24 bytes, so 160 fit in the kernel
 // arguments (a 32-bit length; the host splits longer segments).
@@ -76,6 +78,7 @@ struct SegList {
 };
 static_assert(sizeof(SegList) <= 4096, "the segment list must fit the kernel arguments");
 static_assert(kMaxPiece % kChunk == 0, "pieces are whole chunks");
+static_assert(kMaxPiece / kChunk <= kMaxLaunchChunks, "a piece fits one launch");
 
 __device__ __forceinline__ int find_seg(const SegList& L, int64_t c) {
   int lo = 0, hi = L.count - 1;  // last segment whose first_chunk <= c
@@ -141,7 +144,7 @@ sbp_status launch_segments(const char* who, const std::vector<Seg>& segs, hipStr
       const int64_t ch = (len + kChunk - 1) / kChunk;
       const bool cut_early =
           !one_launch && L.count >= kSegsPerLaunchWhenSplit && L.chunks >= kBigLaunchChunks;
-      if (L.count == kMaxSegs || cut_early || L.chunks + ch > INT32_MAX) {
+      if (L.count == kMaxSegs || cut_early || L.chunks + ch > kMaxLaunchChunks) {
         sbp_status st = flush();
         if (st != SBP_OK) return st;
       }

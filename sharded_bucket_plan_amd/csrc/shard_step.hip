@@ -668,7 +668,8 @@ sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n, floa
   if (out == nullptr) return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: out is null");
   if (!sbp::aligned(out, 16))
     return sbp::fail(SBP_EALIGN, "sbp_reduce_shard: out not 16-B aligned");
-  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_reduce_shard: n too large");
+  if (n > SBP_MAX_SHARD_NUMEL)
+    return sbp::fail(SBP_ERANGE, "sbp_reduce_shard: n above SBP_MAX_SHARD_NUMEL");
   for (int32_t r = 0; r < R; ++r)
     if (sbp::overlaps(out, 4 * n, peers[r], 2 * n))
       return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: out overlaps a peer");
@@ -696,7 +697,8 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers, int32_t R,
   if (acc == nullptr) return sbp::fail(SBP_EINVAL, "sbp_accumulate_grads: acc is null");
   if (!sbp::aligned(acc, 16))
     return sbp::fail(SBP_EALIGN, "sbp_accumulate_grads: acc not 16-B aligned");
-  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_accumulate_grads: n too large");
+  if (n > SBP_MAX_SHARD_NUMEL)
+    return sbp::fail(SBP_ERANGE, "sbp_accumulate_grads: n above SBP_MAX_SHARD_NUMEL");
   for (int32_t r = 0; r < R; ++r)
     if (sbp::overlaps(acc, 4 * n, peers[r], 2 * n))
       return sbp::fail(SBP_EINVAL, "sbp_accumulate_grads: acc overlaps a peer");
@@ -737,7 +739,7 @@ sbp_status check_fused(const char* who, const void* const* peers, int32_t R, con
   for (const void* p : dev)
     if (p != nullptr && !sbp::aligned(p, 16))
       return sbp::fail(SBP_EALIGN, w + ": device pointers must be 16-byte aligned");
-  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, w + ": n too large");
+  if (n > SBP_MAX_SHARD_NUMEL) return sbp::fail(SBP_ERANGE, w + ": n above SBP_MAX_SHARD_NUMEL");
   // pairwise disjoint: acc, master, m, v, param_out and the peers
   const void* ptr[5 + SBP_MAX_PEERS];
   int64_t len[5 + SBP_MAX_PEERS];
@@ -886,7 +888,8 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
     return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: null workspace or result pointer");
   if (!sbp::aligned(sq_out, 8) || !sbp::aligned(workspace, 8))
     return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: workspace and result must be 8-byte aligned");
-  if (n > INT64_MAX / 4) return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm: n too large");
+  if (n > SBP_MAX_SHARD_NUMEL)
+    return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm: n above SBP_MAX_SHARD_NUMEL");
   const int64_t need = sq_norm_workspace(n);
   if (workspace_len < need)
     return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: workspace too small (see "

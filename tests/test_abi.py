@@ -25,6 +25,13 @@ def _declared():
 
 def test_header_and_binding_agree():
     assert sorted(sbp.EXPORTS) == _declared()
+    src = open(os.path.join(ROOT, "include", "sbp.h")).read()
+    defs = dict(re.findall(r"#define (SBP_[A-Z_]+) \(?(-?\d+)(?:LL|u)?\)?", src))
+    assert int(defs["SBP_MAX_SHARD_NUMEL"]) == sbp.MAX_SHARD_NUMEL
+    assert int(defs["SBP_MAX_PEERS"]) == sbp.SBP_MAX_PEERS
+    assert int(defs["SBP_MAX_GROUPS"]) == sbp.MAX_GROUPS
+    for name in ("SBP_OK", "SBP_EINVAL", "SBP_EALIGN", "SBP_ERANGE", "SBP_EHIP", "SBP_ENOMEM"):
+        assert int(defs[name]) == getattr(sbp, name), name
 
 
 def test_library_exports_every_declared_symbol():
@@ -154,6 +161,13 @@ def test_device_calls_validate_before_launch():
     assert acc(None, peers, 2, 16, 1, None) == sbp.SBP_EINVAL
     assert acc(V(0x300008), peers, 2, 16, 1, None) == sbp.SBP_EALIGN
     assert acc(V(0x300000), peers, 2, 0, 0, None) == sbp.SBP_OK
+    # one launch covers at most 2^24 - 1 tiles of 2048 elements
+    big = sbp.MAX_SHARD_NUMEL
+    assert big == (2 ** 24 - 1) * 2048
+    assert call(n=big + 1) == sbp.SBP_ERANGE
+    assert call(n=big) == sbp.SBP_EINVAL  # in range; the fake buffers then overlap
+    assert red(peers, 2, big + 1, 1.0, V(0x300000), None) == sbp.SBP_ERANGE
+    assert acc(V(0x300000), peers, 2, big + 1, 1, None) == sbp.SBP_ERANGE
 
     plan = sbp.bucket_plan([10, 20], 1 << 20, 1)
     grads = (V * 2)(0x100000, 0x200000)
@@ -208,6 +222,9 @@ def test_grad_sq_norm_validates_before_launch():
     assert f(peers, 2, None, 1.0, n, V(0x100000), ws, need, sq, None) == sbp.SBP_EINVAL
     assert f(peers, 2, None, 1.0, n, None, ws, need, V(0x800000), None) == sbp.SBP_EINVAL
     assert f(peers, 2, None, 1.0, -1, None, ws, need, sq, None) == sbp.SBP_EINVAL
+    big = sbp.MAX_SHARD_NUMEL + 1
+    assert f(peers, 2, None, 1.0, big, None, ws, sbp.grad_sq_norm_workspace(big), sq,
+             None) == sbp.SBP_ERANGE
 
 
 def _same_split_plan(numels, cap, N, align=8, order="reverse"):
