@@ -451,3 +451,39 @@ def test_c_client_plan_matches_oracle(tmp_path, name, flags):
     want += [f"state {s} {OP.state_bytes(o.flat_numel, o.shard_numel, s)}" for s in range(4)]
     want += ["einval message", ""]
     assert lines[1:] == want
+
+
+def test_threads_plan_and_keep_their_own_errors():
+    """Plans are built and queried from several threads at once (ctypes
+    releases the GIL, so the calls overlap in the library); each thread reads
+    back the error message of its own last failing call."""
+    import threading
+    w = synth.WORKLOADS["gpt2_small"]
+    want = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    L = sbp.lib()
+    errors = []
+    barrier = threading.Barrier(8)
+
+    def work(k):
+        try:
+            barrier.wait()
+            for it in range(40):
+                p = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+                assert p.num_buckets == len(want.buckets) and p.shard_numel == want.shard_numel
+                assert p.bucket(it % p.num_buckets)["chunk"] == want.buckets[it % p.num_buckets].chunk
+                out = ctypes.c_void_p()
+                if k % 2:  # odd threads fail on the cap, even threads on the world size
+                    st = L.sbp_bucket_plan(None, 0, 0, 1, 8, 0, ctypes.byref(out))
+                    assert st == sbp.SBP_EINVAL and b"bucket_cap_bytes" in L.sbp_last_error()
+                else:
+                    st = L.sbp_bucket_plan(None, 0, 1, 0, 8, 0, ctypes.byref(out))
+                    assert st == sbp.SBP_EINVAL and b"world_n" in L.sbp_last_error()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    ts = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors[:3]

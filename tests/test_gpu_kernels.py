@@ -802,3 +802,52 @@ def test_bf16_emit_structured_sweep():
     H.assert_bits_equal(want[3][~nan], OS.f32_to_bf16(th[~nan]), "oracle emit is the cast")
     pn = got_p[nan].astype(np.uint32) << 16
     assert np.all(np.isnan(pn.view(np.float32))), "NaN emits a NaN"
+
+
+def test_two_threads_two_streams():
+    """Two host threads, each on its own stream (default priority), step their
+    own shards at the same time.  The kernel configuration is one no other
+    test uses (R = 11 with an accumulator), so its first launches, which raise
+    the kernel's LDS limit, also race.  Each thread's result equals the
+    oracle's bit for bit."""
+    import threading
+    import torch
+    n, R, steps = 256 * 8 * 37 + 5, 11, 4
+    jobs = []
+    for k in range(2):
+        th, m, v = _state(60 + k, n)
+        dev = [H.from_np_f32(x) for x in (th, m, v)] + [H.empty_u16(n)]
+        acc_h = (np.random.default_rng(k).normal(size=n) * 1e-3).astype(np.float32)
+        jobs.append(dict(seed=60 + k, host=(th, m, v), dev=dev, acc_h=acc_h,
+                         acc=H.from_np_f32(acc_h), stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def work(j):
+        try:
+            with torch.cuda.stream(j["stream"]):
+                bufs = None
+                barrier.wait()
+                for t in range(1, steps + 1):
+                    bufs = H.dev_peers(j["seed"], t, 0, R, n, 1e-3, bufs)
+                    sbp.adamw_shard(bufs, j["acc"], 0.05, *j["dev"], HP, t)
+                j["stream"].synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    ts = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j in jobs:
+        want = j["host"] + (None,)
+        for t in range(1, steps + 1):
+            want = OS.shard_step(H.host_peers(j["seed"], t, 0, R, n, 1e-3), j["acc_h"],
+                                 np.float32(0.05), want[0], want[1], want[2], HP, t)
+        got = tuple(H.to_np_f32(x) for x in j["dev"][:3]) + (H.to_np_u16(j["dev"][3]),)
+        worst = H.assert_state_close(got, want, f"thread seed {j['seed']}")
+        assert worst == 0, f"expected bit-exact, worst {worst} ulp"
