@@ -25,7 +25,9 @@ Other modes print their own JSON: --layout times pack / shard_of /
 gather_shards / unpack_params / unpack_shards and the plan builds on the workload's model
 (--plan whole | split | per_tensor picks the layout); --bucket-sweep times one
 accumulate pass per bucket for caps of 1..256 MiB on the 7.5B shard;
---calibrate-copy and --summarize-pmc make the HBM-counter summary.
+--stream-mix times the library's kernels against their mix of read and
+write streams on the Llama shard; --calibrate-copy and --summarize-pmc make
+the HBM-counter summary.
 
 The roofline object is for the fused kernel: algorithmic bytes per launch
 ((26 + 2R) bytes per element, +4 with an fp32 accumulator) over its average
@@ -565,6 +567,90 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
             "buckets": pl.num_buckets}
 
 
+def stream_mix(seed, passes=6, reps=5):
+    """Achieved HBM bandwidth of the library's own kernels against their mix of
+    read and write streams, on the Llama-3-8B shard (n = 1,003,782,656): the
+    squared-norm pass (reads only), one-tensor pack (a plain copy), reduce,
+    accumulate and the fused step at several R.  Every configuration is timed
+    round-robin in one process (`passes` rounds of `reps` launches each, HIP
+    events on the launch stream, median), so all share one placement of the
+    arrays.  Algorithmic bytes per element as in the roofline table."""
+    import statistics as st
+    import torch
+    import sharded_bucket_plan_amd as sbp
+    import synth
+
+    w = synth.WORKLOADS["llama3_8b"]
+    n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+    dev = torch.device("cuda:0")
+    peers = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
+                                   synth.peer_stream(1, 0, r), 1e-3) for r in range(8)]
+    f32 = lambda: torch.zeros(n, dtype=torch.float32, device=dev)
+    acc, m, v, out = f32(), f32(), f32(), f32()
+    master = synth.dev_normal_f32(torch.empty(n, dtype=torch.float32, device=dev), seed,
+                                  synth.master_stream(0), 0.02)
+    p = torch.empty(n, dtype=torch.int16, device=dev)
+    flat = torch.empty(n, dtype=torch.int16, device=dev)
+    one = sbp.bucket_plan([n], 4 * n, 1)  # one tensor, one bucket: pack is a plain copy
+    ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=dev)
+    sq = torch.empty(1, dtype=torch.float64, device=dev)
+    hp = sbp.AdamW()
+    t = [0]
+
+    def fused(R, with_acc):
+        def f():
+            t[0] += 1
+            sbp.adamw_shard(peers[:R], acc if with_acc else None, 0.125, master, m, v, p, hp, t[0])
+        return f
+
+    # (name, read streams, write streams, bytes per element, call)
+    kinds = [
+        ("squared norm, R=1", 1, 0, 2, lambda: sbp.grad_sq_norm(peers[:1], None, 1.0, n,
+                                                                workspace=ws, sq_out=sq)),
+        ("squared norm, R=8", 8, 0, 16, lambda: sbp.grad_sq_norm(peers, None, 0.125, n,
+                                                                 workspace=ws, sq_out=sq)),
+        ("squared norm, R=8 + accumulator", 9, 0, 20,
+         lambda: sbp.grad_sq_norm(peers, acc, 0.125, n, workspace=ws, sq_out=sq)),
+        ("pack of one tensor (copy)", 1, 1, 4, lambda: sbp.pack_grads(one, [peers[0]], flat)),
+        ("reduce, R=1", 1, 1, 6, lambda: sbp.reduce_shard(peers[:1], 1.0, out)),
+        ("reduce, R=8", 8, 1, 20, lambda: sbp.reduce_shard(peers, 0.125, out)),
+        ("squared norm, R=8, writing G", 8, 1, 20,
+         lambda: sbp.grad_sq_norm(peers, None, 0.125, n, g_sum_out=out, workspace=ws, sq_out=sq)),
+        ("accumulate, R=8, first", 8, 1, 20,
+         lambda: sbp.accumulate_grads(acc, peers, first=True)),
+        ("accumulate, R=8, later", 9, 1, 24,
+         lambda: sbp.accumulate_grads(acc, peers, first=False)),
+        ("fused step from G (R=0)", 4, 4, 30, fused(0, True)),
+        ("fused step, R=2", 5, 4, 30, fused(2, False)),
+        ("fused step, R=8 (the headline)", 11, 4, 42, fused(8, False)),
+        ("fused step, R=8 + accumulator", 12, 4, 46, fused(8, True)),
+    ]
+    times = {k[0]: [] for k in kinds}
+    torch.cuda.synchronize()
+    for ps in range(passes):
+        for name, _, _, _, f in kinds:
+            for _ in range(2):
+                f()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for a, b in evs:
+                a.record()
+                f()
+                b.record()
+            torch.cuda.synchronize()
+            times[name] += [a.elapsed_time(b) for a, b in evs]
+        log(f"stream mix: pass {ps + 1} of {passes} done")
+    rows = []
+    for name, rd, wr, bpe, _ in kinds:
+        ms = st.median(times[name])
+        gbs = bpe * n / (ms * 1e-3) / 1e9
+        rows.append({"kind": name, "read_streams": rd, "write_streams": wr,
+                     "bytes_per_elem": bpe, "ms_median": ms, "gbs": gbs, "frac": gbs / PEAK_GBS})
+        log(f"stream mix: {name:34s} {rd:2d}R+{wr}W {bpe:2d} B {ms:.3f} ms {gbs:.0f} GB/s "
+            f"{100 * gbs / PEAK_GBS:.1f}%")
+    return {"stream_mix": rows, "n": n, "passes": passes, "reps": reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -588,6 +674,9 @@ def main():
     ap.add_argument("--plan", choices=["whole", "split", "per_tensor"], default="whole",
                     help="with --layout: the plan whose layout is timed (whole-tensor buckets, "
                          "fixed-size split buckets, or one bucket per tensor with row shards)")
+    ap.add_argument("--stream-mix", action="store_true",
+                    help="only time the library's kernels against their read/write stream mix "
+                         "on the Llama-3-8B shard and print their JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5,
@@ -616,6 +705,9 @@ def main():
         return
     if args.layout:
         print(json.dumps(layout_moves(seed, args.workload, args.plan)), flush=True)
+        return
+    if args.stream_mix:
+        print(json.dumps(stream_mix(seed)), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
