@@ -346,6 +346,93 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, command)
     print("\n".join(lines))
 
 
+# Workloads of the per-kernel counter summary: (run name, workload, bench flags)
+PMC_KERNEL_RUNS = (
+    ("dp", "llama3_8b_dp", "--workload llama3_8b_dp --steps 2 --warmup 1"),
+    ("clip", "llama3_8b", "--clip 1.0 --steps 3 --warmup 1"),
+    ("b7", "gpt_7b5", "--workload gpt_7b5 --steps 3 --warmup 1"),
+)
+
+
+def _kernel_read_write(name, R):
+    """Algorithmic (read, write) bytes per element of a kernel, from the
+    template arguments in its rocprofv3 name, or None for a kernel that is
+    not the library's (input generators, torch fills)."""
+    import re
+    m = re.search(r"(fused_adamw_kernel|accumulate_kernel|sq_norm_kernel|reduce_kernel)"
+                  r"<(\d+)(?:, (true|false))?(?:, (true|false))?>", name)
+    if not m:
+        return None
+    kind, r = m.group(1), int(m.group(2))
+    a = m.group(3) == "true"
+    b = m.group(4) == "true"
+    if kind == "fused_adamw_kernel":  # <R, acc, grouped>
+        return 2 * r + 12 + (4 if a else 0), 14
+    if kind == "accumulate_kernel":  # <R, first>
+        return 2 * r + (0 if a else 4), 4
+    if kind == "sq_norm_kernel":  # <R, acc, write>; the tile partials are left out
+        return 2 * r + (4 if a else 0), 4 if b else 0
+    return 2 * r, 4  # reduce_kernel<R>
+
+
+def summarize_pmc_kernels(base, command):
+    """Counted HBM traffic of every library kernel in three workloads against
+    its algorithmic bytes, from rocprofv3 --pmc runs under `base`
+    ({run}_FETCH_SIZE and {run}_WRITE_SIZE per entry of PMC_KERNEL_RUNS, and
+    cal_FETCH_SIZE / cal_WRITE_SIZE of --calibrate-copy).  Dispatches of one
+    kernel are summed and divided by the steps the run made (warm-up
+    included); copy_kernel's algorithmic bytes are the pack's 4 per element."""
+    import synth
+    import sharded_bucket_plan_amd as sbp
+
+    cf = sum(x for _, x in _pmc_rows(os.path.join(base, "cal_FETCH_SIZE"), "FETCH_SIZE"))
+    cw = sum(x for _, x in _pmc_rows(os.path.join(base, "cal_WRITE_SIZE"), "WRITE_SIZE"))
+    known = CALIBRATION_CALLS * COPY_BYTES
+    fs, ws = known / (cf * 1024), known / (cw * 1024)
+    lines = ["# HBM traffic of every library kernel against its algorithmic bytes", "",
+             "Commands (rocprofv3, one counter per run; R is the repository root on the GPU box):",
+             "", "```", command, "```", "",
+             f"Calibration (4 GiB copies, {CALIBRATION_CALLS} calls): bytes read = 1024 x "
+             f"FETCH_SIZE x {fs:.4f}, bytes written = 1024 x WRITE_SIZE x {ws:.4f}.  "
+             "Per step: the kernel's dispatches "
+             "summed over the run, divided by its steps (warm-up included).  The squared-norm "
+             "pass also writes one 8-byte partial per 2048-element tile, which its algorithmic "
+             "bytes leave out.", "",
+             "| workload | kernel | dispatches | read GB counted / algorithmic | "
+             "written GB counted / algorithmic |", "|---|---|---|---|---|"]
+    for run, wl, flags in PMC_KERNEL_RUNS:
+        w = synth.WORKLOADS[wl]
+        n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+        steps = int(flags.split("--steps ")[1].split()[0]) + int(flags.split("--warmup ")[1].split()[0])
+        F, W = {}, {}
+        for k, x in _pmc_rows(os.path.join(base, f"{run}_FETCH_SIZE"), "FETCH_SIZE"):
+            F.setdefault(k, []).append(x)
+        for k, x in _pmc_rows(os.path.join(base, f"{run}_WRITE_SIZE"), "WRITE_SIZE"):
+            W.setdefault(k, []).append(x)
+        for k in sorted(F):
+            if "copy_kernel" in k:
+                rd, wr, short = 2, 2, "copy_kernel (pack)"
+            else:
+                rw = _kernel_read_write(k, w.R)
+                if rw is None:
+                    continue
+                rd, wr = rw
+                short = k.split("(anonymous namespace)::")[1].split("(")[0] if \
+                    "(anonymous namespace)::" in k else k
+            per = 1.0 / steps
+            got_r = sum(F[k]) * 1024 * fs * per
+            got_w = sum(W.get(k, [0.0])) * 1024 * ws * per
+            # a pack covers the flat buffer once per step, in however many launches
+            launches = 1 if "copy_kernel" in k else len(F[k]) / steps
+            alg_r, alg_w = rd * n * launches, wr * n * launches
+            wcell = f"{got_w / 1e9:.3f} / {alg_w / 1e9:.3f} = {got_w / alg_w:.4f}" if alg_w \
+                else f"{got_w / 1e9:.4f} / 0"
+            lines.append(f"| {wl} | `{short}` | {len(F[k])} | {got_r / 1e9:.3f} / {alg_r / 1e9:.3f}"
+                         f" = {got_r / alg_r:.4f} | {wcell} |")
+    lines += ["", f"source_sha256 (shard_step.hip and its build flags): {kernel_source_hash()}"]
+    return "\n".join(lines) + "\n"
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -679,6 +766,9 @@ def main():
                          "on the Llama-3-8B shard and print their JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 4 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-pmc-kernels", nargs=2, metavar=("BASE_DIR", "CMD"),
+                    help="print the per-kernel HBM-traffic summary from the counter runs "
+                         "under BASE_DIR")
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "CMD"),
                     help="write the HBM-traffic summary from rocprofv3 counter runs")
@@ -686,6 +776,9 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_pmc_kernels:
+        print(summarize_pmc_kernels(*args.summarize_pmc_kernels), end="")
         return
 
     if args.gpus != 1:

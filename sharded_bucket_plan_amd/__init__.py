@@ -275,9 +275,15 @@ def tokens_scale(counts):
 # ---- device calls ------------------------------------------------------------
 
 def _stream(stream, tensor):
+    """The HIP stream of a call: the given one, else the current stream of the
+    current device.  The library launches on the current HIP device, so the
+    call's tensors must live there."""
+    import torch
+    if tensor.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {tensor.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; select it with torch.cuda.device")
     if stream is not None:
         return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
-    import torch
     return ctypes.c_void_p(torch.cuda.current_stream(tensor.device).cuda_stream)
 
 
