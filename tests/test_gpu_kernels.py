@@ -89,13 +89,11 @@ def _state(seed, n):
     return th, np.zeros(n, np.float32), np.zeros(n, np.float32)
 
 
-@pytest.mark.parametrize("R", [1, 2, 4, 7, 8, 16])
-@pytest.mark.parametrize("n", SIZES + [BIG])
+# every peer count at the small sizes; the multi-pass size at R = 8
+@pytest.mark.parametrize("R,n", [(R, n) for R in [1, 2, 4, 7, 8, 16] for n in SIZES] + [(8, BIG)])
 @pytest.mark.parametrize("with_acc", [False, True])
 def test_adamw_shard(R, n, with_acc):
     import torch
-    if n == BIG and R not in (8,):
-        pytest.skip("big size runs at R=8 only")
     steps = 3
     th, m, v = _state(14, n)
     gs = [H.guarded_from(x) for x in (th, m, v)]
@@ -165,13 +163,10 @@ def _elem_groups(starts, groups, n):
     return g
 
 
-@pytest.mark.parametrize("R", [0, 1, 8])
-@pytest.mark.parametrize("n", SIZES + [BIG])
+@pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 8] for n in SIZES] + [(8, BIG)])
 def test_adamw_shard_grouped(R, n):
     """Per-group lr and weight decay from a run table, every element."""
     import torch
-    if n == BIG and R != 8:
-        pytest.skip("big size runs at R=8 only")
     rng = np.random.default_rng(n * 31 + R)
     starts, groups = _random_runs(n, rng)
     eg = _elem_groups(starts, groups, n)
@@ -468,13 +463,11 @@ def test_layout_segment_longer_than_2_30():
 
 # ---- global gradient-norm clipping ---------------------------------------------
 
-@pytest.mark.parametrize("R", [0, 1, 3, 8])
-@pytest.mark.parametrize("n", [1, 9, 2047, 256 * 8 * 3 + 5, BIG])
+@pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 3, 8]
+                                  for n in [1, 9, 2047, 256 * 8 * 3 + 5]] + [(8, BIG)])
 @pytest.mark.parametrize("write", [False, True])
 def test_grad_sq_norm(R, n, write):
     import torch
-    if n == BIG and R not in (8,):
-        pytest.skip("big size runs at R=8 only")
     bufs = H.dev_peers(21, 1, 0, R, n, 1e-3) if R else []
     acc_d = None
     acc_h = None
