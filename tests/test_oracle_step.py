@@ -70,6 +70,21 @@ def test_bf16_cast_matches_torch_structured_sweep():
     assert np.array_equal(ours[nan] >> 15, (u[nan] >> 31).astype(np.uint16))
 
 
+def test_bf16_cast_exhaustive():
+    """Every one of the 2^32 fp32 bit patterns: the oracle's cast equals
+    torch's round-to-nearest-even conversion, NaNs compared by class and
+    sign (torch returns one canonical NaN).  256 blocks of 2^24 patterns in
+    spawned worker processes (about half a minute on 8 cores)."""
+    import multiprocessing as mp
+    import os
+    from tests import cast_sweep
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(cast_sweep.check_block, range((1 << 32) // cast_sweep.BLOCK))
+    assert sum(r[0] for r in res) == 0, "non-NaN patterns that round differently"
+    assert sum(r[1] for r in res) == 0, "NaN patterns that lose their class or sign"
+
+
 def test_bf16_widen_exact():
     b = np.arange(65536, dtype=np.uint16)
     w = S.bf16_to_f32(b)
