@@ -191,6 +191,70 @@ def test_llama3_8b_shard_sampled():
         H.assert_bits_equal(a, b, f"llama3_8b {name}")
 
 
+def test_llama3_8b_grouped_sampled():
+    """The Llama-3-8B shard with the benchmark's two parameter groups (decay on
+    matrices, none on the 1-D tensors; bench.py --groups): two grouped steps,
+    sampled elements.  A sampled element's group is that of the tensor owning
+    its flat position under the oracle's plan (rank 0 owns chunk 0 of every
+    bucket; this plan has no padding); the sample adds the first and last
+    shard element of every 1-D tensor piece, so both groups and every group
+    boundary are in it."""
+    import torch
+    w = synth.WORKLOADS["llama3_8b"]
+    hp = _hp(w)
+    tg = [1 if len(shape) == 1 else 0 for _, shape in w.params]
+    groups = [(hp.lr, hp.weight_decay), (hp.lr, 0.0)]
+    pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    opl = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    n = pl.shard_numel
+    rs, rg = sbp.group_table(pl, 0, tg, H.dev())
+    f32 = lambda: torch.empty(n, dtype=torch.float32, device=H.dev())
+    dth, dm, dv = f32(), f32(), f32()
+    synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+    dm.zero_()
+    dv.zero_()
+    dp = H.empty_u16(n)
+    # shard positions of rank 0 <-> flat positions, from the oracle plan
+    so = np.array([b.shard_offset for b in opl.buckets], np.int64)
+    fo = np.array([b.flat_offset for b in opl.buckets], np.int64)
+    ch = np.array([b.chunk for b in opl.buckets], np.int64)
+    extra = []
+    for t, (_, shape) in enumerate(w.params):
+        if len(shape) != 1:
+            continue
+        a = opl.tensor_flat_offset(t)
+        e = a + w.numels[t]
+        for b in range(len(opl.buckets)):  # rank 0's chunk of bucket b: [fo, fo + ch)
+            lo, hi = max(a, fo[b]), min(e, fo[b] + ch[b])
+            if lo < hi:
+                extra += [so[b] + lo - fo[b], so[b] + hi - 1 - fo[b]]
+    idx = np.unique(np.concatenate([_sample_index(pl, n, 1 << 18, 4),
+                                    np.array(extra, np.int64)]))
+    bk = np.searchsorted(so, idx, side="right") - 1
+    flat = fo[bk] + (idx - so[bk])
+    starts = np.array([opl.tensor_flat_offset(t) for t in range(len(w.numels))], np.int64)
+    order = np.argsort(starts)
+    tids = order[np.searchsorted(starts[order], flat, side="right") - 1]
+    assert np.all(flat - starts[tids] < np.array(w.numels)[tids])  # no padding
+    elem_group = np.array(tg, np.int64)[tids]
+    assert set(np.unique(elem_group)) == {0, 1}
+    th = synth.normal_f32_at(SEED, synth.master_stream(0), idx, w.master_sigma)
+    want = (th, np.zeros_like(th), np.zeros_like(th), None)
+    bufs = None
+    for t in (1, 2):
+        bufs = H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, bufs)
+        sbp.adamw_shard_grouped(bufs, None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t,
+                                groups, rs, rg)
+        peers_h = [synth.normal_bf16_at(SEED, synth.peer_stream(t, 0, r), idx, w.grad_sigma)
+                   for r in range(w.R)]
+        want = OS.shard_step_grouped(peers_h, None, OS.mean_scale(w.R), want[0], want[1],
+                                     want[2], hp, groups, elem_group, t)
+    torch.cuda.synchronize()
+    got = _sampled_state(dth, dm, dv, dp, idx)
+    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
+        H.assert_bits_equal(a, b, f"llama3_8b grouped {name}")
+
+
 def test_gpt_7b5_accumulate_tokens_sampled():
     """'7.5B'-labelled GPT shard (N=64, R=8): 4 microbatches, the first three
     accumulated bucket by bucket, the last fused; 1/C valid-token scaling."""
