@@ -324,7 +324,9 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers,
  * master,m,v device fp32[n], updated in place
  * param_out  device bf16[n] (the all-gather send buffer)
  * hp         hyperparameters; hp->step = t >= 1 (1-based, once per
- *            optimizer step, not per microbatch)
+ *            optimizer step, not per microbatch); beta1 and beta2 in
+ *            [0, 1); lr, eps and weight_decay finite and >= 0 (the ranges
+ *            torch.optim.AdamW accepts); SBP_EINVAL otherwise
  * All device pointers 16-byte aligned and pairwise non-overlapping.
  * Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL),
  * SBP_EHIP.
@@ -364,7 +366,8 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R,
  *   supplies beta1, beta2, eps and step (its lr and weight_decay are not
  *   used).  A group id outside 0..n_groups-1 in the table uses group 0.
  *   Other arguments, layout and errors as in sbp_adamw_shard, plus:
- *   groups      host array of n_groups (1..SBP_MAX_GROUPS) entries
+ *   groups      host array of n_groups (1..SBP_MAX_GROUPS) entries, each
+ *               lr and weight_decay finite and >= 0
  *   run_start   device int64[n_runs], 8-B aligned, ascending, starting at 0
  *   run_group   device int32[n_runs], 4-B aligned
  *   n_runs      >= 1 (the table from sbp_group_runs, copied to the device)

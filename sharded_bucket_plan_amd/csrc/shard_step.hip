@@ -41,6 +41,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <mutex>
 #include <set>
 #include <string>
@@ -719,6 +720,17 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers, int32_t R,
 
 namespace {
 
+// Hyperparameter ranges, as torch.optim.AdamW checks them (a NaN fails every
+// comparison): betas in [0, 1) keep the bias corrections positive, and lr,
+// eps and weight decay are finite and >= 0.
+bool valid_betas_eps(const sbp_adamw_hparams& hp) {
+  return hp.beta1 >= 0.0f && hp.beta1 < 1.0f && hp.beta2 >= 0.0f && hp.beta2 < 1.0f &&
+         hp.eps >= 0.0f && std::isfinite(hp.eps);
+}
+bool valid_lr_wd(float lr, float wd) {
+  return lr >= 0.0f && std::isfinite(lr) && wd >= 0.0f && std::isfinite(wd);
+}
+
 // Checks shared by the fused entry points; fills P.
 sbp_status check_fused(const char* who, const void* const* peers, int32_t R, const float* acc,
                        float* master, float* m, float* v, void* param_out, int64_t n,
@@ -728,6 +740,8 @@ sbp_status check_fused(const char* who, const void* const* peers, int32_t R, con
   if (n < 0) return sbp::fail(SBP_EINVAL, w + ": n < 0");
   if (hp == nullptr) return sbp::fail(SBP_EINVAL, w + ": hp is null");
   if (hp->step < 1) return sbp::fail(SBP_EINVAL, w + ": step must be >= 1");
+  if (!valid_betas_eps(*hp))
+    return sbp::fail(SBP_EINVAL, w + ": beta1 and beta2 must be in [0, 1), eps finite and >= 0");
   if (n == 0) return SBP_OK;
   sbp_status st = collect_peers(who, peers, R, P);
   if (st != SBP_OK) return st;
@@ -791,6 +805,8 @@ sbp_status sbp_adamw_shard(const void* const* peers, int32_t R, const float* acc
   Peers P;
   sbp_status st = check_fused(who, peers, R, acc, master, m, v, param_out, n, hp, P);
   if (st != SBP_OK) return st;
+  if (!valid_lr_wd(hp->lr, hp->weight_decay))
+    return sbp::fail(SBP_EINVAL, "sbp_adamw_shard: lr and weight_decay must be finite and >= 0");
   if (n == 0) return sbp::ok();  // nothing is read or written
   const GroupArgs none{};
   double bc1, bc2;
@@ -814,6 +830,11 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R, const fl
     return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: groups is null");
   if (n_groups < 1 || n_groups > SBP_MAX_GROUPS)
     return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: n_groups must be in 1..8");
+  for (int32_t k = 0; k < n_groups; ++k)
+    if (!valid_lr_wd(groups[k].lr, groups[k].weight_decay))
+      return sbp::fail(SBP_EINVAL,
+                       "sbp_adamw_shard_grouped: each group's lr and weight_decay must be "
+                       "finite and >= 0");
   if (n_runs < 1) return sbp::fail(SBP_EINVAL, "sbp_adamw_shard_grouped: n_runs must be >= 1");
   if (n == 0) return sbp::ok();  // nothing is read or written
   if (run_start == nullptr || run_group == nullptr)

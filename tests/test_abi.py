@@ -145,6 +145,18 @@ def test_device_calls_validate_before_launch():
     bad_hp = sbp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0)
     assert call(hp=ctypes.byref(bad_hp)) == sbp.SBP_EINVAL
     assert call(hp=None) == sbp.SBP_EINVAL
+    # hyperparameter ranges: betas in [0, 1), lr, eps and weight decay finite and >= 0
+    inf, nan = float("inf"), float("nan")
+    for fields in [(1e-3, 1.0, 0.999, 1e-8, 0.01), (1e-3, 0.9, 1.0, 1e-8, 0.01),
+                   (1e-3, -0.1, 0.999, 1e-8, 0.01), (1e-3, nan, 0.999, 1e-8, 0.01),
+                   (1e-3, 0.9, 0.999, -1e-8, 0.01), (1e-3, 0.9, 0.999, inf, 0.01),
+                   (-1e-3, 0.9, 0.999, 1e-8, 0.01), (inf, 0.9, 0.999, 1e-8, 0.01),
+                   (1e-3, 0.9, 0.999, 1e-8, -0.01), (1e-3, 0.9, 0.999, 1e-8, nan)]:
+        h = sbp.AdamWHParams(*fields, 1)
+        assert call(hp=ctypes.byref(h)) == sbp.SBP_EINVAL, fields
+        assert call(hp=ctypes.byref(h), n=0) == sbp.SBP_EINVAL, fields
+    edge = sbp.AdamWHParams(0.0, 0.0, 0.0, 0.0, 0.0, 1)  # the low ends are allowed
+    assert call(hp=ctypes.byref(edge), n=0) == sbp.SBP_OK
     assert call(m=V(0x300000 + 1024)) == sbp.SBP_EINVAL  # overlaps master
     assert call(p=V(0x100000 + 512)) == sbp.SBP_EINVAL  # overlaps a peer
     assert call(n=0) == sbp.SBP_OK  # nothing to do, nothing launched
@@ -424,6 +436,14 @@ def test_grouped_step_validates_before_launch():
     assert call(m=V(0x300000 + 1024)) == sbp.SBP_EINVAL
     assert call(n=0) == sbp.SBP_OK
     assert call(n=0, rs=None, rg=None) == sbp.SBP_OK
+    # each group's lr and weight decay finite and >= 0 (hp's own are not used)
+    bad = (sbp.GroupHParams * 2)(sbp.GroupHParams(1e-3, 0.1), sbp.GroupHParams(-1e-3, 0.0))
+    assert call(groups=bad) == sbp.SBP_EINVAL
+    bad = (sbp.GroupHParams * 2)(sbp.GroupHParams(1e-3, float("nan")), sbp.GroupHParams(1e-3, 0))
+    assert call(groups=bad) == sbp.SBP_EINVAL
+    assert call(groups=bad, ng=1) == sbp.SBP_EINVAL
+    unused = sbp.AdamWHParams(-1.0, 0.9, 0.999, 1e-8, -5.0, 1)
+    assert call(hp=ctypes.byref(unused), n=0) == sbp.SBP_OK
 
 
 @pytest.mark.parametrize("name,flags", [("tiny_mlp", 0), ("gpt2_small", 0), ("gpt2_small", 1),
