@@ -253,7 +253,8 @@ int main(int argc, char** argv) {
   for (int it = 0; it < iters; ++it) {
     Case c;
     c.kind = static_cast<int>(rng() % 3);
-    c.N = 1 + static_cast<int32_t>(rng() % 5);
+    c.N = rng() % 8 == 0 ? static_cast<int32_t>(std::vector<int>{8, 17, 64}[rng() % 3])
+                         : 1 + static_cast<int32_t>(rng() % 5);
     c.align = static_cast<int32_t>(std::vector<int>{1, 2, 8}[rng() % 3]);
     c.cap = static_cast<int64_t>(std::vector<int>{2, 16, 64, 200, 1 << 20}[rng() % 5]);
     const int32_t T = static_cast<int32_t>(rng() % 9);

@@ -541,12 +541,12 @@ def test_clipped_step_two_shards(max_norm):
 
 # ---- layout moves: pack / unpack / shard_of / gather on both plan kinds ---------
 
-@pytest.mark.parametrize("kind", ["whole", "split", "per_tensor"])
+@pytest.mark.parametrize("kind,N", [("whole", 4), ("split", 4), ("per_tensor", 4),
+                                    ("whole", 64), ("split", 64), ("per_tensor", 64)])
 @pytest.mark.parametrize("misalign", [False, True])
-def test_layout_moves(kind, misalign):
+def test_layout_moves(kind, N, misalign):
     import torch
     numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
-    N = 4
     if kind == "per_tensor":
         rows = [37, 8, 1, 13, 1, 16, 9, 25, 3, 400, 1]
         pl = sbp.bucket_plan_per_tensor(numels, N, rows)
