@@ -589,6 +589,12 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     tensors = [torch.empty(k, dtype=torch.int16, device=dev) for k in w.numels]
     for t, x in enumerate(tensors):
         synth.dev_normal_bf16(x, seed, synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
+    tset = sbp.TensorSet(pl, tensors)  # the same buffers, marshalled once
+    one_pass = {
+        "pack_grads": lambda: sbp.pack_grads(pl, tset, flat),
+        "unpack_params": lambda: sbp.unpack_params(pl, flat, tset),
+        "unpack_shards": lambda: sbp.unpack_shards(pl, shards, tset),
+    }
     calls = {
         "pack_grads": (lambda: sbp.pack_grads(pl, tensors, flat), 4 * P + 2 * (F - P)),
         "shard_of": (lambda: sbp.shard_of(pl, 0, flat, shards[0]), 4 * n),
@@ -632,8 +638,14 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
         out[name] = {"ms_median": med, "call_ms_median": call, "algorithmic_bytes": nbytes,
                      "gbs": nbytes / (med * 1e-3) / 1e9,
                      "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_GBS}
+        if name in one_pass:  # the per-tensor pointers from a TensorSet
+            one_pass[name]()
+            torch.cuda.synchronize()
+            out[name]["call_ms_median_tensorset"] = timed(one_pass[name])
         log(f"layout: {name} {med:.3f} ms on the GPU ({out[name]['gbs']:.0f} GB/s), "
-            f"{call:.3f} ms per Python call")
+            f"{call:.3f} ms per Python call"
+            + (f", {out[name]['call_ms_median_tensorset']:.3f} ms with a TensorSet"
+               if name in one_pass else ""))
     # the plans themselves (host only, made once per model): microseconds per build
     plans = {}
     for name, make in (("bucket_plan", lambda: sbp.bucket_plan(w.numels, w.bucket_cap_bytes,

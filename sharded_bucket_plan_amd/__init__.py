@@ -10,6 +10,7 @@ Functions (same names as the C calls without the "sbp_" prefix):
   plans        bucket_plan (whole-tensor or split buckets), bucket_plan_per_tensor
                (one bucket per tensor, dim-0 row shards), Plan queries
   layout       pack_grads, unpack_params, shard_of, gather_shards, unpack_shards
+               (+ TensorSet: a plan's per-tensor buffers marshalled once)
   scales       mean_scale, tokens_scale, clip_scale
   shard step   reduce_shard, accumulate_grads, adamw_shard, grad_sq_norm
                (+ grad_sq_norm_workspace)
@@ -308,28 +309,68 @@ def _ptrs(tensors, what):
     return (ctypes.c_void_p * max(len(tensors), 1))(*[_dev(t, 2, what) for t in tensors])
 
 
+class TensorSet:
+    """One 2-byte device tensor per plan tensor, marshalled once.
+
+    Gradient and parameter buffers usually live for the whole run: building
+    their pointer array once takes the per-call work (a size check and a
+    data pointer per tensor) out of pack_grads, unpack_params and
+    unpack_shards, which accept a TensorSet wherever they take a list.  The
+    set holds references to its tensors.  None entries stay null and may only
+    stand for tensors outside the buckets a call selects."""
+
+    def __init__(self, plan, tensors):
+        T, _, _ = plan._cached_sizes()
+        if len(tensors) != T:
+            raise ValueError("TensorSet: one tensor per plan tensor")
+        self.plan = plan
+        self.tensors = list(tensors)
+        self.array = (ctypes.c_void_p * max(T, 1))()
+        for t, x in enumerate(self.tensors):
+            if x is None:
+                continue
+            if x.numel() != plan.numels[t]:
+                raise ValueError(f"TensorSet: tensor {t} has {x.numel()} elements")
+            if x.numel():
+                self.array[t] = _dev(x, 2, "TensorSet")
+
+
+def _tensor_array(plan, tensors, bucket, what):
+    """Host array of per-tensor device pointers for a layout call on `bucket`:
+    a TensorSet's own array, or one marshalled from a list (only the tensors
+    the call touches are read; None allowed for the others)."""
+    if isinstance(tensors, TensorSet):
+        if tensors.plan is not plan:
+            raise ValueError(f"{what}: the TensorSet was built for another plan")
+        return tensors.array
+    T, _, _ = plan._cached_sizes()
+    if len(tensors) != T:
+        raise ValueError(f"{what}: one tensor per plan tensor")
+    arr = (ctypes.c_void_p * max(T, 1))()
+    for t in plan._tensors_of(int(bucket)):
+        x = tensors[t]
+        if x is None:
+            continue
+        if x.numel() != plan.numels[t]:
+            raise ValueError(f"{what}: tensor {t} has {x.numel()} elements")
+        if x.numel():
+            arr[t] = _dev(x, 2, what)
+    return arr
+
+
 def pack_grads(plan, grads, flat, bucket=-1, stream=None):
     """sbp_pack_grads: copy per-tensor bf16 grads into the flat buckets (+0 elsewhere).
 
     grads: one 2-byte device tensor per plan tensor (None allowed for tensors
-    outside the selected bucket); flat: 2-byte device tensor of plan.flat_numel.
+    outside the selected bucket), or a TensorSet; flat: 2-byte device tensor
+    of plan.flat_numel.
     """
-    T, F, _ = plan._cached_sizes()
-    if len(grads) != T:
-        raise ValueError("pack_grads: one gradient per plan tensor")
+    _, F, _ = plan._cached_sizes()
     if flat.numel() != F:
         raise ValueError("pack_grads: flat has the wrong size")
     if bucket >= plan.num_buckets:
         raise SbpError(SBP_EINVAL, "pack_grads: bucket out of range")
-    arr = (ctypes.c_void_p * max(T, 1))()
-    for t in plan._tensors_of(int(bucket)):  # only the tensors the call reads
-        g = grads[t]
-        if g is None:
-            continue
-        if g.numel() != plan.numels[t]:
-            raise ValueError(f"pack_grads: tensor {t} has {g.numel()} elements")
-        if g.numel():
-            arr[t] = _dev(g, 2, "pack_grads grads")
+    arr = _tensor_array(plan, grads, bucket, "pack_grads grads")
     _check(lib().sbp_pack_grads(plan.handle, int(bucket), arr, _dev(flat, 2, "pack_grads flat"),
                                 _stream(stream, flat)))
 
@@ -487,23 +528,13 @@ def unpack_params(plan, flat, params, bucket=-1, stream=None):
     """sbp_unpack_params: flat bf16 buckets -> per-tensor bf16 parameters.
 
     params: one 2-byte device tensor per plan tensor (None allowed outside the
-    selected bucket)."""
-    T, F, _ = plan._cached_sizes()
-    if len(params) != T:
-        raise ValueError("unpack_params: one parameter per plan tensor")
+    selected bucket), or a TensorSet."""
+    _, F, _ = plan._cached_sizes()
     if flat.numel() != F:
         raise ValueError("unpack_params: flat has the wrong size")
     if bucket >= plan.num_buckets:
         raise SbpError(SBP_EINVAL, "unpack_params: bucket out of range")
-    arr = (ctypes.c_void_p * max(T, 1))()
-    for t in plan._tensors_of(int(bucket)):  # only the tensors the call reads
-        p = params[t]
-        if p is None:
-            continue
-        if p.numel() != plan.numels[t]:
-            raise ValueError(f"unpack_params: tensor {t} has {p.numel()} elements")
-        if p.numel():
-            arr[t] = _dev(p, 2, "unpack_params params")
+    arr = _tensor_array(plan, params, bucket, "unpack_params params")
     _check(lib().sbp_unpack_params(plan.handle, int(bucket), _dev(flat, 2, "unpack_params flat"),
                                    arr, _stream(stream, flat)))
 
@@ -531,24 +562,13 @@ def unpack_shards(plan, shards, params, bucket=-1, stream=None):
     one pass (gather_shards followed by unpack_params, without the flat buffer).
 
     params: one 2-byte device tensor per plan tensor (None allowed outside the
-    selected bucket)."""
-    T, _, _ = plan._cached_sizes()
+    selected bucket), or a TensorSet."""
     if len(shards) != plan.world_n:
         raise ValueError("unpack_shards: one shard per rank")
     if any(x.numel() != plan.shard_numel for x in shards):
         raise ValueError("unpack_shards: a shard has the wrong size")
-    if len(params) != T:
-        raise ValueError("unpack_shards: one parameter per plan tensor")
     if bucket >= plan.num_buckets:
         raise SbpError(SBP_EINVAL, "unpack_shards: bucket out of range")
-    arr = (ctypes.c_void_p * max(T, 1))()
-    for t in plan._tensors_of(int(bucket)):  # only the tensors the call writes
-        p = params[t]
-        if p is None:
-            continue
-        if p.numel() != plan.numels[t]:
-            raise ValueError(f"unpack_shards: tensor {t} has {p.numel()} elements")
-        if p.numel():
-            arr[t] = _dev(p, 2, "unpack_shards params")
+    arr = _tensor_array(plan, params, bucket, "unpack_shards params")
     _check(lib().sbp_unpack_shards(plan.handle, int(bucket), _ptrs(shards, "unpack_shards shards"),
                                    arr, _stream(stream, shards[0])))

@@ -844,3 +844,51 @@ def test_two_threads_two_streams():
         got = tuple(H.to_np_f32(x) for x in j["dev"][:3]) + (H.to_np_u16(j["dev"][3]),)
         worst = H.assert_state_close(got, want, f"thread seed {j['seed']}")
         assert worst == 0, f"expected bit-exact, worst {worst} ulp"
+
+
+def test_tensor_set_paths():
+    """Per-tensor buffers marshalled once (TensorSet) give the same bytes as
+    the list form in pack_grads, unpack_params and unpack_shards, whole and
+    bucket by bucket, over repeated calls; a set built for another plan or
+    with a wrongly sized tensor is refused."""
+    import torch
+    numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
+    N = 4
+    pl = sbp.bucket_plan(numels, 600, N)
+    grads_h = [synth.normal_bf16(33, synth.tensor_stream(1, 0, 0, t), k, 1e-2)
+               for t, k in enumerate(numels)]
+    gd = [H.from_np_u16(h) if h.size else H.empty_u16(0) for h in grads_h]
+    gs = sbp.TensorSet(pl, gd)
+    want_flat = OS.pack(OP.bucket_plan(numels, 600, N), grads_h)
+    for rep in range(2):
+        flat = H.empty_u16(pl.flat_numel)
+        flat.fill_(0x1111)
+        if rep == 0:
+            sbp.pack_grads(pl, gs, flat)
+        else:
+            for b in range(pl.num_buckets):
+                sbp.pack_grads(pl, gs, flat, bucket=b)
+        torch.cuda.synchronize()
+        H.assert_bits_equal(H.to_np_u16(flat), want_flat, f"pack with a TensorSet, pass {rep}")
+    outs = [H.empty_u16(k) for k in numels]
+    os_ = sbp.TensorSet(pl, outs)
+    sbp.unpack_params(pl, flat, os_)
+    torch.cuda.synchronize()
+    for t, h in enumerate(grads_h):
+        H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack with a TensorSet, tensor {t}")
+    shards = [H.empty_u16(pl.shard_numel) for _ in range(N)]
+    for s in range(N):
+        sbp.shard_of(pl, s, flat, shards[s])
+    for x in outs:
+        x.fill_(0)
+    sbp.unpack_shards(pl, shards, os_)
+    torch.cuda.synchronize()
+    for t, h in enumerate(grads_h):
+        H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack_shards with a TensorSet, tensor {t}")
+    other = sbp.bucket_plan(numels, 600, N)
+    with pytest.raises(ValueError):
+        sbp.pack_grads(other, gs, flat)
+    with pytest.raises(ValueError):
+        sbp.TensorSet(pl, gd[:-1])
+    with pytest.raises(ValueError):
+        sbp.TensorSet(pl, gd[:-1] + [H.empty_u16(5)])
