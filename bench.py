@@ -360,7 +360,7 @@ def _kernel_read_write(name, R):
     not the library's (input generators, torch fills)."""
     import re
     m = re.search(r"(fused_adamw_kernel|accumulate_kernel|sq_norm_kernel|reduce_kernel)"
-                  r"<(\d+)(?:, (true|false))?(?:, (true|false))?>", name)
+                  r"<(\d+)(?:, (true|false))?(?:, (true|false))?(?:, \d+)?>", name)
     if not m:
         return None
     kind, r = m.group(1), int(m.group(2))
@@ -706,6 +706,10 @@ def stream_mix(seed, passes=6, reps=5):
     kinds = [
         ("squared norm, R=1", 1, 0, 2, lambda: sbp.grad_sq_norm(peers[:1], None, 1.0, n,
                                                                 workspace=ws, sq_out=sq)),
+        ("squared norm, R=2", 2, 0, 4, lambda: sbp.grad_sq_norm(peers[:2], None, 0.5, n,
+                                                                workspace=ws, sq_out=sq)),
+        ("squared norm of the accumulator (R=0)", 1, 0, 4,
+         lambda: sbp.grad_sq_norm([], acc, 0.125, n, workspace=ws, sq_out=sq)),
         ("squared norm, R=8", 8, 0, 16, lambda: sbp.grad_sq_norm(peers, None, 0.125, n,
                                                                  workspace=ws, sq_out=sq)),
         ("squared norm, R=8 + accumulator", 9, 0, 20,

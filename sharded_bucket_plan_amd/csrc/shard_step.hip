@@ -416,35 +416,49 @@ __device__ __forceinline__ double block_sum(double x) {
   return t;
 }
 
-template <int R, bool ACC, bool WRITE>
+// GPL groups of 8 per lane (a tile of 2048 * GPL elements): the light
+// configurations (16 or 32 bytes of loads per group) take 4 or 2 so a CU can
+// keep enough loads in flight; all of a lane's loads are issued first, and
+// its groups are summed in order.
+template <int R, bool ACC, bool WRITE, int GPL>
 __global__ void __launch_bounds__(kBlock)
 sq_norm_kernel(Peers P, const float* __restrict__ acc, float scale, float* __restrict__ gsum,
                int64_t n, double* __restrict__ partial) {
   static_assert(R > 0 || ACC, "R == 0 needs the accumulator");
   const int64_t groups = n >> 3;
-  const int64_t gi = my_group();
+  const int64_t g0 = static_cast<int64_t>(my_tile()) * kBlock * GPL + threadIdx.x;
   double local = 0.0;
-  if (gi < groups) {
-    u32x4 w[R > 0 ? R : 1];
-    if constexpr (R > 0) load_peers<R>(P, gi, w);
-    float A[8];
-    if (ACC) load8(acc, gi, A);
-    float G[8];
-    if constexpr (R > 0) {
-      peer_sum8<R>(w, G);
-      if (ACC) {
+  u32x4 w[GPL][R > 0 ? R : 1];
+  float A[GPL][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) G[j] = A[j] + G[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) G[j] = A[j];
+  for (int q = 0; q < GPL; ++q) {
+    const int64_t gi = g0 + static_cast<int64_t>(q) * kBlock;
+    if (gi < groups) {
+      if constexpr (R > 0) load_peers<R>(P, gi, w[q]);
+      if (ACC) load8(acc, gi, A[q]);
     }
-    if (WRITE) store8(gsum, gi, G);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double g = static_cast<double>(G[j] * scale);
-      local = local + g * g;
+  for (int q = 0; q < GPL; ++q) {
+    const int64_t gi = g0 + static_cast<int64_t>(q) * kBlock;
+    if (gi < groups) {
+      float G[8];
+      if constexpr (R > 0) {
+        peer_sum8<R>(w[q], G);
+        if (ACC) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) G[j] = A[q][j] + G[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) G[j] = A[q][j];
+      }
+      if (WRITE) store8(gsum, gi, G);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double g = static_cast<double>(G[j] * scale);
+        local = local + g * g;
+      }
     }
   }
   if (blockIdx.x == 0) {
@@ -524,8 +538,8 @@ int64_t tiles_for(int64_t n) {
 
 // One block per 2048-element tile; `lane_bytes` = bytes one lane loads;
 // blocks per CU capped to keep about `inflight_kb` KiB of loads in flight.
-Launch launch_for(int64_t n, int lane_bytes, int inflight_kb) {
-  Launch L{static_cast<unsigned>(tiles_for(n)), 0};
+Launch launch_for(int64_t n, int lane_bytes, int inflight_kb, int gpl = 1) {
+  Launch L{static_cast<unsigned>((tiles_for(n) + gpl - 1) / gpl), 0};
   const DeviceInfo d = device_info();
   if (inflight_kb > 0 && d.lds_per_cu > 0) {
     const int64_t per_block = static_cast<int64_t>(lane_bytes) * kBlock;
@@ -638,8 +652,8 @@ Scalars adamw_scalars(const sbp_adamw_hparams& hp, double bc1, double bc2, float
 // `lane_bytes` and `inflight_kb`.
 template <typename K, typename... Args>
 sbp_status launch_capped(const char* who, K kernel, int64_t n, int lane_bytes, int inflight_kb,
-                         hipStream_t stream, Args... args) {
-  const Launch L = launch_for(n, lane_bytes, inflight_kb);
+                         int gpl, hipStream_t stream, Args... args) {
+  const Launch L = launch_for(n, lane_bytes * gpl, inflight_kb, gpl);
   sbp_status st = allow_lds(kernel, L.lds);
   if (st != SBP_OK) return st;
   hipLaunchKernelGGL(kernel, dim3(L.grid), dim3(kBlock), L.lds, stream, args...);
@@ -649,7 +663,7 @@ sbp_status launch_capped(const char* who, K kernel, int64_t n, int lane_bytes, i
 template <typename K, typename... Args>
 sbp_status launch(const char* who, K kernel, int64_t n, int lane_bytes, hipStream_t stream,
                   Args... args) {
-  return launch_capped(who, kernel, n, lane_bytes, SBP_INFLIGHT_KB, stream, args...);
+  return launch_capped(who, kernel, n, lane_bytes, SBP_INFLIGHT_KB, 1, stream, args...);
 }
 
 }  // namespace
@@ -866,6 +880,13 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R, const fl
   return launch_fused<true>(who, P, R, acc, scale, master, m, v, param_out, n, s, ga, stream);
 }
 
+// Groups of 8 per lane of the squared-norm pass for `lane_bytes` of loads per
+// group: 4 at 16 bytes (one bf16 peer), 2 at 32 bytes (two peers, or the
+// accumulator alone), else 1 -- the same choice as the dispatch below.
+static int norm_groups_per_lane(int lane_bytes) {
+  return lane_bytes == 16 ? 4 : lane_bytes == 32 ? 2 : 1;
+}
+
 // Workspace of the squared norm: the tile partials, then each tree level.
 static int64_t sq_norm_workspace(int64_t n) {
   int64_t count = tiles_for(n), total = count;
@@ -940,25 +961,29 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
     for (int b = a + 1; b < k; ++b)
       if (sbp::overlaps(ptr[a], len[a], ptr[b], len[b]))
         return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: buffers overlap");
-  const int lane_bytes = 16 * R + (acc ? 32 : 0);
+  const int lane_bytes = 16 * R + (acc ? 32 : 0);  // per group of 8
+  const int gpl = norm_groups_per_lane(lane_bytes);
   constexpr int kNormInflight = SBP_NORM_INFLIGHT_KB;
   st = dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
     const bool wr = g_sum_out != nullptr;
-    auto go = [&](auto kernel) {
-      return launch_capped(who, kernel, n, lane_bytes, kNormInflight, stream, P, acc, scale,
+    auto go = [&](auto kernel, int g) {
+      return launch_capped(who, kernel, n, lane_bytes, kNormInflight, g, stream, P, acc, scale,
                            g_sum_out, n, workspace);
     };
-    if constexpr (RR == 0) {
-      return wr ? go(sq_norm_kernel<0, true, true>) : go(sq_norm_kernel<0, true, false>);
+    if constexpr (RR == 0) {  // 32 bytes per group
+      return wr ? go(sq_norm_kernel<0, true, true, 2>, 2) : go(sq_norm_kernel<0, true, false, 2>, 2);
     } else if (acc) {
-      return wr ? go(sq_norm_kernel<RR, true, true>) : go(sq_norm_kernel<RR, true, false>);
+      return wr ? go(sq_norm_kernel<RR, true, true, 1>, 1)
+                : go(sq_norm_kernel<RR, true, false, 1>, 1);
     } else {
-      return wr ? go(sq_norm_kernel<RR, false, true>) : go(sq_norm_kernel<RR, false, false>);
+      constexpr int G = RR == 1 ? 4 : RR == 2 ? 2 : 1;  // 16, 32 bytes per group
+      return wr ? go(sq_norm_kernel<RR, false, true, G>, G)
+                : go(sq_norm_kernel<RR, false, false, G>, G);
     }
   });
   if (st != SBP_OK) return st;
-  return sum_partials(who, workspace, tiles_for(n), sq_out, stream);
+  return sum_partials(who, workspace, (tiles_for(n) + gpl - 1) / gpl, sq_out, stream);
 }
 
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale, float* clipped_scale,

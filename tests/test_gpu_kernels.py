@@ -463,8 +463,10 @@ def test_layout_segment_longer_than_2_30():
 
 # ---- global gradient-norm clipping ---------------------------------------------
 
-@pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 3, 8]
-                                  for n in [1, 9, 2047, 256 * 8 * 3 + 5]] + [(8, BIG)])
+# R = 1 and R = 2 without an accumulator, and R = 0, take 4 / 2 / 2 groups per lane
+@pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 2, 3, 8]
+                                  for n in [1, 9, 2047, 256 * 8 * 3 + 5, 256 * 8 * 9 + 3]]
+                         + [(8, BIG), (1, BIG), (2, BIG), (0, BIG)])
 @pytest.mark.parametrize("write", [False, True])
 def test_grad_sq_norm(R, n, write):
     import torch
