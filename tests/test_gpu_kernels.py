@@ -412,6 +412,35 @@ def test_pack_big_tensors_many_launches():
     H.assert_bits_equal(H.to_np_u16(flat), OS.pack(opl, gh), "pack big")
 
 
+@pytest.mark.parametrize("align", [8, 1])
+def test_many_small_tensors(align):
+    """5,000 small tensors (0-300 elements) at N = 8: thousands of copy
+    segments, so many launches filled up to 160 small segments each; pack,
+    then the shards straight into per-tensor buffers, against the oracle."""
+    import torch
+    rng = np.random.default_rng(align)
+    numels = [int(x) for x in rng.integers(0, 301, 5000)]
+    N = 8
+    pl = sbp.bucket_plan(numels, 64 << 10, N, align)
+    opl = OP.bucket_plan(numels, 64 << 10, N, align)
+    gh = [synth.normal_bf16(35, synth.tensor_stream(1, 0, 0, t), k, 1e-2)
+          for t, k in enumerate(numels)]
+    gd = [H.from_np_u16(h) if h.size else H.empty_u16(0) for h in gh]
+    flat = H.empty_u16(pl.flat_numel)
+    sbp.pack_grads(pl, gd, flat)
+    want = OS.pack(opl, gh)
+    shards = [H.empty_u16(pl.shard_numel) for _ in range(N)]
+    for s in range(N):
+        sbp.shard_of(pl, s, flat, shards[s])
+    outs = [H.empty_u16(k) for k in numels]
+    sbp.unpack_shards(pl, shards, outs)
+    torch.cuda.synchronize()
+    H.assert_bits_equal(H.to_np_u16(flat), want, "pack of 5,000 tensors")
+    for t, h in enumerate(gh):
+        if h.size:
+            H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack_shards tensor {t}")
+
+
 def test_layout_segment_longer_than_2_30():
     """A tensor of more than 2^30 elements: its copy segment is split into
     pieces for the kernel (whose segment length is 32-bit).  Pack, unpack and
