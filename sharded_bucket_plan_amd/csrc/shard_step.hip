@@ -85,6 +85,7 @@ constexpr bool kNtStore = SBP_NT_STORE != 0;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 __device__ __forceinline__ T ldg(const T* p) {
@@ -312,7 +313,95 @@ accumulate_kernel(Peers P, float* __restrict__ acc, int64_t n) {
 }
 
 // ---- fused: G = [acc +] S, g = G*scale, AdamW, bf16 emit --------------------
-// GROUPED: step size and decay per element from the run table in `ga`.
+// Plain step with R <= 2 (one parameter group): the lane-to-element map is
+// "split" -- lane l of wave w takes elements [w*512 + 4l, +4) and
+// [w*512 + 256 + 4l, +4) of its tile -- so each 16-byte fp32 load or store
+// instruction of a wave covers one contiguous kilobyte (with 8 consecutive
+// elements per lane, an instruction touches every other 16 bytes of 2 KB),
+// and each 8-byte bf16 one covers 512 contiguous bytes.  Measured on the
+// 1.0B shard, round-robin in two processes against 8 consecutive elements
+// per lane: R = 2 +1.0 / +2.1 points of 8 TB/s, the update from G (R = 0)
+// +0.9 / +1.4.  With R = 8 the same map needs twice the peer load
+// instructions and measured 0.5 points slower; moving the peer sums through
+// LDS instead (16-byte peer loads) gained under 0.4 points, so R >= 3 keeps
+// 8 consecutive elements per lane.
+__device__ __forceinline__ void bf16x4(u32x2 u, float (&x)[4]) {
+  x[0] = bf16_lo(u.x);
+  x[1] = bf16_hi(u.x);
+  x[2] = bf16_lo(u.y);
+  x[3] = bf16_hi(u.y);
+}
+
+template <int R, bool ACC>
+__device__ __forceinline__ void fused_split_tile(const Peers& P, const float* __restrict__ acc,
+                                                 float scale, float* __restrict__ master,
+                                                 float* __restrict__ mom1,
+                                                 float* __restrict__ mom2,
+                                                 uint16_t* __restrict__ pout, int64_t n,
+                                                 const Scalars& s) {
+  static_assert(R <= 2, "the split map is for light peer counts");
+  const int64_t full = (n >> 3) << 3;  // elements in whole groups of 8
+  const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+  const int64_t tile0 = static_cast<int64_t>(my_tile()) * (kBlock * 8);
+  const int64_t e[2] = {tile0 + wv * 512 + ln * 4, tile0 + wv * 512 + 256 + ln * 4};
+  // a run of 4 lies wholly inside or outside [0, full): full is a multiple of 8
+  const bool ok[2] = {e[0] < full, e[1] < full};
+  u32x2 w[2][R > 0 ? R : 1];
+  f32x4 A[2], T[2], M[2], V[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (ok[c]) {
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[c][r] = ldg(reinterpret_cast<const u32x2*>(P.p[r] + e[c]));
+      }
+      if (ACC) A[c] = ldg(reinterpret_cast<const f32x4*>(acc + e[c]));
+      T[c] = ldg(reinterpret_cast<const f32x4*>(master + e[c]));
+      M[c] = ldg(reinterpret_cast<const f32x4*>(mom1 + e[c]));
+      V[c] = ldg(reinterpret_cast<const f32x4*>(mom2 + e[c]));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (ok[c]) {
+      float G[4];
+      if constexpr (R > 0) {
+        bf16x4(w[c][0], G);
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+          float x[4];
+          bf16x4(w[c][r], x);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) G[j] = G[j] + x[j];
+        }
+        if (ACC) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) G[j] = A[c][j] + G[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) G[j] = A[c][j];
+      }
+      float th[4], m[4], v[4];
+      uint32_t pb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        th[j] = T[c][j];
+        m[j] = M[c][j];
+        v[j] = V[c][j];
+        adamw_one(G[j] * scale, th[j], m[j], v[j], s);
+        pb[j] = bf16_rne(th[j]);
+      }
+      stg(reinterpret_cast<f32x4*>(master + e[c]), f32x4{th[0], th[1], th[2], th[3]});
+      stg(reinterpret_cast<f32x4*>(mom1 + e[c]), f32x4{m[0], m[1], m[2], m[3]});
+      stg(reinterpret_cast<f32x4*>(mom2 + e[c]), f32x4{v[0], v[1], v[2], v[3]});
+      stg(reinterpret_cast<u32x2*>(pout + e[c]), u32x2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)});
+    }
+  }
+}
+
+// R >= 3 or GROUPED: 8 consecutive elements per lane.  GROUPED: step size
+// and decay per element from the run table in `ga`.
 template <int R, bool ACC, bool GROUPED>
 __global__ void __launch_bounds__(kBlock)
 fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
@@ -321,53 +410,57 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
                    Scalars s, GroupArgs ga) {
   static_assert(R > 0 || ACC, "R == 0 needs the accumulator");
   const int64_t groups = n >> 3;
-  const int64_t gi = my_group();
-  if (gi < groups) {
-    u32x4 w[R > 0 ? R : 1];
-    if constexpr (R > 0) load_peers<R>(P, gi, w);
-    float A[8], th[8], m[8], v[8];
-    if (ACC) load8(acc, gi, A);
-    load8(master, gi, th);
-    load8(mom1, gi, m);
-    load8(mom2, gi, v);
-    float G[8];
-    if constexpr (R > 0) {
-      peer_sum8<R>(w, G);
-      if (ACC) {
+  if constexpr (!GROUPED && R <= 2) {
+    fused_split_tile<R, ACC>(P, acc, scale, master, mom1, mom2, pout, n, s);
+  } else {
+    const int64_t gi = my_group();
+    if (gi < groups) {
+      u32x4 w[R > 0 ? R : 1];
+      if constexpr (R > 0) load_peers<R>(P, gi, w);
+      float A[8], th[8], m[8], v[8];
+      if (ACC) load8(acc, gi, A);
+      load8(master, gi, th);
+      load8(mom1, gi, m);
+      load8(mom2, gi, v);
+      float G[8];
+      if constexpr (R > 0) {
+        peer_sum8<R>(w, G);
+        if (ACC) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) G[j] = A[j] + G[j];
+          for (int j = 0; j < 8; ++j) G[j] = A[j] + G[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) G[j] = A[j];
       }
-    } else {
+      uint32_t pb[8];
+      if constexpr (GROUPED) {
+        float ss[8], dc[8];
+        group_scalars8(ga, (gi - threadIdx.x) * 8, gi * 8, ss, dc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) G[j] = A[j];
+        for (int j = 0; j < 8; ++j) {
+          Scalars sj = s;
+          sj.step_size = ss[j];
+          sj.decay = dc[j];
+          adamw_one(G[j] * scale, th[j], m[j], v[j], sj);
+          pb[j] = bf16_rne(th[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          adamw_one(G[j] * scale, th[j], m[j], v[j], s);
+          pb[j] = bf16_rne(th[j]);
+        }
+      }
+      store8(master, gi, th);
+      store8(mom1, gi, m);
+      store8(mom2, gi, v);
+      stg(reinterpret_cast<u32x4*>(pout) + gi,
+          u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                pb[6] | (pb[7] << 16)});
     }
-    uint32_t pb[8];
-    if constexpr (GROUPED) {
-      float ss[8], dc[8];
-      group_scalars8(ga, (gi - threadIdx.x) * 8, gi * 8, ss, dc);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        Scalars sj = s;
-        sj.step_size = ss[j];
-        sj.decay = dc[j];
-        adamw_one(G[j] * scale, th[j], m[j], v[j], sj);
-        pb[j] = bf16_rne(th[j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        adamw_one(G[j] * scale, th[j], m[j], v[j], s);
-        pb[j] = bf16_rne(th[j]);
-      }
-    }
-    store8(master, gi, th);
-    store8(mom1, gi, m);
-    store8(mom2, gi, v);
-    stg(reinterpret_cast<u32x4*>(pout) + gi,
-        u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-              pb[6] | (pb[7] << 16)});
-  }
-  if (blockIdx.x == 0) {
+  }  // GROUPED
+  if (blockIdx.x == 0) {  // the n % 8 tail, element by element
     const int64_t i = (groups << 3) + threadIdx.x;
     if (i < n) {
       float G;
@@ -795,15 +888,16 @@ sbp_status launch_fused(const char* who, const Peers& P, int32_t R, const float*
   (void)hipGetLastError();
   return dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
+    auto go = [&](auto kernel) {
+      return launch(who, kernel, n, lane_bytes, stream, P, acc, scale, master, m, v, pout, n, s,
+                    ga);
+    };
     if constexpr (RR == 0) {
-      return launch(who, fused_adamw_kernel<0, true, GROUPED>, n, lane_bytes, stream, P, acc,
-                    scale, master, m, v, pout, n, s, ga);
+      return go(fused_adamw_kernel<0, true, GROUPED>);
     } else if (acc) {
-      return launch(who, fused_adamw_kernel<RR, true, GROUPED>, n, lane_bytes, stream, P, acc,
-                    scale, master, m, v, pout, n, s, ga);
+      return go(fused_adamw_kernel<RR, true, GROUPED>);
     } else {
-      return launch(who, fused_adamw_kernel<RR, false, GROUPED>, n, lane_bytes, stream, P, acc,
-                    scale, master, m, v, pout, n, s, ga);
+      return go(fused_adamw_kernel<RR, false, GROUPED>);
     }
   });
 }
