@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <cstring>
 #include <mutex>
 #include <set>
 #include <string>
@@ -711,17 +712,40 @@ sbp_status dispatch_r(int32_t R, F&& f) {
 }
 
 // Bias corrections 1 - b1^t and 1 - b2^t in float64 from the binary32 betas;
-// beta^t by t multiplications.
-void bias_corrections(const sbp_adamw_hparams& hp, double& bc1, double& bc2) {
-  const double b1 = hp.beta1, b2 = hp.beta2;
+// beta^t by t multiplications.  A training run calls with t = 1, 2, 3, ...,
+// so the powers of the last call are kept per thread (with the betas they
+// belong to) and extended by the missing multiplications: the same sequence
+// of products, hence the same bits, at O(1) cost per step instead of O(t)
+// (about a millisecond at t = 10^6).  Any other call starts again from 1.
+struct BetaPowers {
+  float b1 = 0.0f, b2 = 0.0f;
+  int64_t t = -1;  // no powers kept yet
   double b1t = 1.0, b2t = 1.0;
-  for (int64_t k = 0; k < hp.step; ++k) {
-    b1t *= b1;
-    b2t *= b2;
-    if (b1t == 0.0 && b2t == 0.0) break;  // both powers have underflowed for good
+};
+thread_local BetaPowers g_beta_powers;
+
+void bias_corrections(const sbp_adamw_hparams& hp, double& bc1, double& bc2) {
+  BetaPowers& c = g_beta_powers;
+  const bool same_betas = std::memcmp(&c.b1, &hp.beta1, sizeof(float)) == 0 &&
+                          std::memcmp(&c.b2, &hp.beta2, sizeof(float)) == 0;
+  if (c.t < 0 || !same_betas || c.t > hp.step) {
+    c.b1 = hp.beta1;
+    c.b2 = hp.beta2;
+    c.t = 0;
+    c.b1t = 1.0;
+    c.b2t = 1.0;
   }
-  bc1 = 1.0 - b1t;
-  bc2 = 1.0 - b2t;
+  const double b1 = hp.beta1, b2 = hp.beta2;
+  for (; c.t < hp.step; ++c.t) {
+    if (c.b1t == 0.0 && c.b2t == 0.0) {  // both powers have underflowed for good
+      c.t = hp.step;
+      break;
+    }
+    c.b1t *= b1;
+    c.b2t *= b2;
+  }
+  bc1 = 1.0 - c.b1t;
+  bc2 = 1.0 - c.b2t;
 }
 
 // Host scalars of one AdamW step: float64 from the binary32 hyperparameters,

@@ -923,3 +923,27 @@ def test_tensor_set_paths():
         sbp.TensorSet(pl, gd[:-1])
     with pytest.raises(ValueError):
         sbp.TensorSet(pl, gd[:-1] + [H.empty_u16(5)])
+
+
+def test_step_counts_in_any_order():
+    """The bias corrections depend only on the step passed, whatever steps
+    earlier calls used (forwards, backwards, repeated, far ahead, another
+    beta), each call checked against the oracle on fresh state."""
+    import torch
+    n, R = 256 * 8 * 2 + 7, 3
+    th0, m0, v0 = _state(71, n)
+    m0 = (np.random.default_rng(1).normal(size=n) * 1e-3).astype(np.float32)
+    v0 = np.abs(np.random.default_rng(2).normal(size=n) * 1e-6).astype(np.float32)
+    peers_h = H.host_peers(71, 1, 0, R, n, 1e-3)
+    peers_d = [H.from_np_u16(x) for x in peers_h]
+    other = sbp.AdamW(1e-3, 0.8, 0.99, 1e-8, 0.01)
+    for t, hp in [(5, HP), (6, HP), (3, HP), (3, HP), (4, HP), (1000, HP), (7, HP),
+                  (7, other), (8, other), (2, HP), (10 ** 6, HP), (10 ** 6 + 1, HP), (1, HP)]:
+        dth, dm, dv = H.from_np_f32(th0), H.from_np_f32(m0), H.from_np_f32(v0)
+        dp = H.empty_u16(n)
+        sbp.adamw_shard(peers_d, None, 0.25, dth, dm, dv, dp, hp, t)
+        torch.cuda.synchronize()
+        want = OS.shard_step(peers_h, None, np.float32(0.25), th0, m0, v0, hp, t)
+        got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+        worst = H.assert_state_close(got, want, f"step {t} betas {hp.beta1}/{hp.beta2}")
+        assert worst == 0, f"step {t}: expected bit-exact, worst {worst} ulp"
