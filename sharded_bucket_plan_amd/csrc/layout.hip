@@ -25,6 +25,13 @@
 //     kernel arguments;
 //   - a chunk is 256 lanes x 16 bytes, fully coalesced, when source and
 //     destination are 16-byte aligned; otherwise element by element.
+// gather and unpack_shards read across the N shards, which as segments is one
+// per rank for every bucket or tensor piece (GPT-2 small under the per-tensor
+// plan: 1,184 segments, eight launches).  They go out as fans instead: the N
+// shard pointers once in the arguments, then one 40-byte piece per bucket or
+// tensor piece naming the bucket positions it covers.  A block whose 2048
+// elements lie in one rank's chunk (every block, when chunks are long) copies
+// as above; otherwise each lane finds its rank from its own position.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,20 +96,9 @@ __device__ __forceinline__ int find_seg(const SegList& L, int64_t c) {
   return lo;
 }
 
-__global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
-  // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
-  unsigned b = blockIdx.x;
-  const unsigned per = gridDim.x / kXcds;
-  if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
-  const int64_t c = b;
-  const DevSeg sg = L.seg[find_seg(L, c)];
-  const int64_t start = (c - sg.first_chunk) * kChunk;
-  const int64_t rem = static_cast<int64_t>(sg.len) - start;
-  const int64_t cnt = rem < kChunk ? rem : kChunk;
-  uint16_t* d = sg.dst + start;
-  const uint16_t* s = sg.src ? sg.src + start : nullptr;
-  const bool vec = (reinterpret_cast<uintptr_t>(sg.dst) & 15) == 0 &&
-                   (s == nullptr || (reinterpret_cast<uintptr_t>(sg.src) & 15) == 0);
+// `cnt` (at most kChunk) elements from s (null: +0) to d, by one block;
+// `vec`: both 16-byte aligned.
+__device__ __forceinline__ void copy_chunk(uint16_t* d, const uint16_t* s, int64_t cnt, bool vec) {
   if (vec) {
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
@@ -116,6 +112,90 @@ __global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
     }
   } else {
     for (int64_t j = threadIdx.x; j < cnt; j += kBlock) d[j] = s ? s[j] : 0;
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
+  // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
+  unsigned b = blockIdx.x;
+  const unsigned per = gridDim.x / kXcds;
+  if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+  const int64_t c = b;
+  const DevSeg sg = L.seg[find_seg(L, c)];
+  const int64_t start = (c - sg.first_chunk) * kChunk;
+  const int64_t rem = static_cast<int64_t>(sg.len) - start;
+  const int64_t cnt = rem < kChunk ? rem : kChunk;
+  const bool vec = (reinterpret_cast<uintptr_t>(sg.dst) & 15) == 0 &&
+                   (sg.src == nullptr || (reinterpret_cast<uintptr_t>(sg.src) & 15) == 0);
+  copy_chunk(sg.dst + start, sg.src ? sg.src + start : nullptr, cnt, vec);
+}
+
+// Fans (the all-gather side): the shard pointers once, then up to kMaxFans
+// pieces, within the argument size the segment list above already uses.
+constexpr int kMaxFans = 83;
+using sbp::FanPiece;
+using sbp::kMaxFanRanks;
+
+struct FanList {
+  const uint16_t* shard[kMaxFanRanks];
+  FanPiece fan[kMaxFans];
+  int32_t count;
+  int32_t chunks;  // total chunks of this launch
+};
+static_assert(sizeof(FanPiece) == 40, "a fan piece is 40 bytes");
+static_assert(sizeof(FanList) <= sizeof(SegList), "fans take no more argument space than segments");
+static_assert(sbp::kFanPiece % kChunk == 0, "pieces are whole chunks");
+static_assert(sbp::kFanPiece / kChunk <= kMaxLaunchChunks, "a piece fits one launch");
+
+__device__ __forceinline__ int find_fan(const FanList& L, int64_t c) {
+  int lo = 0, hi = L.count - 1;  // last piece whose first_chunk <= c
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (L.fan[mid].first_chunk <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kBlock) fan_copy_kernel(FanList L) {
+  // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
+  unsigned b = blockIdx.x;
+  const unsigned per = gridDim.x / kXcds;
+  if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
+  const int64_t c = b;
+  const FanPiece f = L.fan[find_fan(L, c)];
+  const uint32_t start = static_cast<uint32_t>(c - f.first_chunk) * static_cast<uint32_t>(kChunk);
+  const uint32_t rem = static_cast<uint32_t>(f.len) - start;
+  const uint32_t cnt = rem < static_cast<uint32_t>(kChunk) ? rem : static_cast<uint32_t>(kChunk);
+  uint16_t* d = f.dst + start;
+  // offset o of the piece: position t = j0 + o past the start of rank s0's chunk
+  const uint32_t base = static_cast<uint32_t>(f.j0) + start;
+  const uint32_t chunk = static_cast<uint32_t>(f.chunk);
+  const uint32_t q0 = base / chunk;
+  if ((base + cnt - 1) / chunk == q0) {
+    // the block's elements lie in one rank's chunk (every block, when chunks
+    // are long): one shard pointer for the block, a plain copy
+    const uint16_t* s = L.shard[f.s0 + static_cast<int32_t>(q0)] + f.shard_off + (base - q0 * chunk);
+    copy_chunk(d, s, cnt, f.vec != 0);
+    return;
+  }
+  auto src = [&](uint32_t o) {
+    const uint32_t t = base + o;
+    const uint32_t q = t / chunk;
+    return L.shard[f.s0 + static_cast<int32_t>(q)] + f.shard_off + (t - q * chunk);
+  };
+  if (f.vec) {
+    // j0, chunk and the start are multiples of 8: a lane's 8 elements lie in one rank's chunk
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const uint32_t e = static_cast<uint32_t>(k * kBlock * 8) + threadIdx.x * 8;
+      if (e + 8 <= cnt) {
+        *reinterpret_cast<uint4*>(d + e) = *reinterpret_cast<const uint4*>(src(e));
+      } else {
+        for (uint32_t j = e; j < cnt; ++j) d[j] = *src(j);
+      }
+    }
+  } else {
+    for (uint32_t j = threadIdx.x; j < cnt; j += kBlock) d[j] = *src(j);
   }
 }
 
@@ -157,6 +237,51 @@ sbp_status launch_segments(const char* who, const std::vector<Seg>& segs, hipStr
   return st != SBP_OK ? st : sbp::ok();
 }
 
+// The fans in as few launches as their pieces allow, or, when they cannot be
+// expressed as pieces, as plain segments.
+sbp_status launch_fans(const char* who, const sbp_plan* plan, const void* const* shards,
+                       const std::vector<sbp::Fan>& fans, hipStream_t stream) {
+  std::vector<FanPiece> pieces;
+  std::vector<Seg> segs;
+  try {
+    if (!sbp::fan_pieces(fans, plan->world_n, pieces)) {
+      sbp::fans_to_segments(fans, shards, segs);
+      return launch_segments(who, segs, stream);
+    }
+  } catch (...) {
+    return sbp::fail(SBP_ENOMEM, std::string(who) + ": out of host memory");
+  }
+  (void)hipGetLastError();
+  FanList L;
+  for (int32_t r = 0; r < kMaxFanRanks; ++r)
+    L.shard[r] = r < plan->world_n ? static_cast<const uint16_t*>(shards[r]) : nullptr;
+  L.count = 0;
+  L.chunks = 0;
+  auto flush = [&]() -> sbp_status {
+    if (L.count == 0) return SBP_OK;
+    hipLaunchKernelGGL(fan_copy_kernel, dim3(static_cast<unsigned>(L.chunks)), dim3(kBlock), 0,
+                       stream, L);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return sbp::fail(SBP_EHIP, std::string(who) + ": launch failed: " + hipGetErrorString(e));
+    L.count = 0;
+    L.chunks = 0;
+    return SBP_OK;
+  };
+  for (FanPiece p : pieces) {
+    const int64_t ch = (p.len + kChunk - 1) / kChunk;
+    if (L.count == kMaxFans || L.chunks + ch > kMaxLaunchChunks) {
+      sbp_status st = flush();
+      if (st != SBP_OK) return st;
+    }
+    p.first_chunk = L.chunks;
+    L.fan[L.count++] = p;
+    L.chunks += static_cast<int32_t>(ch);
+  }
+  sbp_status st = flush();
+  return st != SBP_OK ? st : sbp::ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,16 +309,16 @@ sbp_status sbp_shard_of(const sbp_plan* plan, int32_t bucket, int32_t rank, cons
 
 sbp_status sbp_gather_shards(const sbp_plan* plan, int32_t bucket, const void* const* shards,
                              void* flat, hipStream_t stream) {
-  std::vector<Seg> segs;
-  sbp_status st = sbp::gather_segments(plan, bucket, shards, flat, segs);
-  return st != SBP_OK ? st : launch_segments("sbp_gather_shards", segs, stream);
+  std::vector<sbp::Fan> fans;
+  sbp_status st = sbp::gather_fans(plan, bucket, shards, flat, fans);
+  return st != SBP_OK ? st : launch_fans("sbp_gather_shards", plan, shards, fans, stream);
 }
 
 sbp_status sbp_unpack_shards(const sbp_plan* plan, int32_t bucket, const void* const* shards,
                              void* const* tensor_params, hipStream_t stream) {
-  std::vector<Seg> segs;
-  sbp_status st = sbp::unpack_shards_segments(plan, bucket, shards, tensor_params, segs);
-  return st != SBP_OK ? st : launch_segments("sbp_unpack_shards", segs, stream);
+  std::vector<sbp::Fan> fans;
+  sbp_status st = sbp::unpack_shards_fans(plan, bucket, shards, tensor_params, fans);
+  return st != SBP_OK ? st : launch_fans("sbp_unpack_shards", plan, shards, fans, stream);
 }
 
 }  // extern "C"

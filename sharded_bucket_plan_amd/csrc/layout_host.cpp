@@ -183,8 +183,8 @@ sbp_status shard_of_segments(const sbp_plan* plan, int32_t bucket, int32_t rank,
   return sbp::ok();
 }
 
-sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
-                           void* flat, std::vector<Seg>& out) {
+sbp_status gather_fans(const sbp_plan* plan, int32_t bucket, const void* const* shards, void* flat,
+                       std::vector<Fan>& out) {
   out.clear();
   const char* who = "sbp_gather_shards";
   if (plan == nullptr || shards == nullptr || flat == nullptr)
@@ -203,26 +203,38 @@ sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* con
   sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
   if (st != SBP_OK) return st;
   uint16_t* F = static_cast<uint16_t*>(flat);
-  std::vector<Seg> segs;
+  std::vector<Fan> fans;
   try {
     for (int32_t b = b0; b < b1; ++b) {
       const sbp::Bucket& k = plan->buckets[b];
-      if (k.chunk == 0) continue;
-      for (int32_t s = 0; s < plan->world_n; ++s)
-        segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + k.shard_offset,
-                           F + k.flat_offset + s * k.chunk, k.chunk});
+      if (k.chunk > 0) fans.push_back(Fan{k.shard_offset, k.chunk, 0, k.padded, F + k.flat_offset});
     }
   } catch (...) {
     return sbp::fail(SBP_ENOMEM, "sbp_gather_shards: out of host memory");
   }
-  out.swap(segs);
+  out.swap(fans);
+  return sbp::ok();
+}
+
+sbp_status gather_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                           void* flat, std::vector<Seg>& out) {
+  out.clear();
+  std::vector<Fan> fans;
+  sbp_status st = gather_fans(plan, bucket, shards, flat, fans);
+  if (st != SBP_OK) return st;
+  try {
+    fans_to_segments(fans, shards, out);
+  } catch (...) {
+    out.clear();
+    return sbp::fail(SBP_ENOMEM, "sbp_gather_shards: out of host memory");
+  }
   return sbp::ok();
 }
 
 // Each tensor piece of a selected bucket is cut where the bucket's rank
 // chunks meet; each cut part is read from the shard of the rank that owns it.
-sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
-                                  void* const* tensor_params, std::vector<Seg>& out) {
+sbp_status unpack_shards_fans(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                              void* const* tensor_params, std::vector<Fan>& out) {
   out.clear();
   const char* who = "sbp_unpack_shards";
   if (plan == nullptr || shards == nullptr || tensor_params == nullptr)
@@ -236,7 +248,7 @@ sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const vo
   int64_t lo, hi;
   sbp_status st = bucket_range(who, plan, bucket, &b0, &b1, &lo, &hi);
   if (st != SBP_OK) return st;
-  std::vector<Seg> segs;
+  std::vector<Fan> fans;
   try {
     std::vector<std::pair<uintptr_t, int64_t>> outs;
     std::vector<char> seen(plan->numel.size(), 0);
@@ -257,14 +269,9 @@ sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const vo
           outs.push_back({reinterpret_cast<uintptr_t>(dst), bytes});
           seen[pc.t] = 1;
         }
-        const int64_t rel = pc.flat - k.flat_offset;  // piece start inside the bucket
-        for (int64_t s = rel / k.chunk; s * k.chunk < rel + pc.len; ++s) {
-          const int64_t a = std::max(rel, s * k.chunk);
-          const int64_t e = std::min(rel + pc.len, (s + 1) * k.chunk);
-          segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + k.shard_offset +
-                                 (a - s * k.chunk),
-                             static_cast<uint16_t*>(dst) + pc.elem + (a - rel), e - a});
-        }
+        // the piece's positions in the bucket, read from the ranks that own them
+        fans.push_back(Fan{k.shard_offset, k.chunk, pc.flat - k.flat_offset, pc.len,
+                           static_cast<uint16_t*>(dst) + pc.elem});
       }
     }
     if (!disjoint(outs))
@@ -272,9 +279,61 @@ sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const vo
   } catch (...) {
     return sbp::fail(SBP_ENOMEM, "sbp_unpack_shards: out of host memory");
   }
-  out.swap(segs);
+  out.swap(fans);
   return sbp::ok();
 }
+
+sbp_status unpack_shards_segments(const sbp_plan* plan, int32_t bucket, const void* const* shards,
+                                  void* const* tensor_params, std::vector<Seg>& out) {
+  out.clear();
+  std::vector<Fan> fans;
+  sbp_status st = unpack_shards_fans(plan, bucket, shards, tensor_params, fans);
+  if (st != SBP_OK) return st;
+  try {
+    fans_to_segments(fans, shards, out);
+  } catch (...) {
+    out.clear();
+    return sbp::fail(SBP_ENOMEM, "sbp_unpack_shards: out of host memory");
+  }
+  return sbp::ok();
+}
+
+void fans_to_segments(const std::vector<Fan>& fans, const void* const* shards,
+                      std::vector<Seg>& segs) {
+  for (const Fan& f : fans) {
+    for (int64_t x = f.x0; x < f.x0 + f.len;) {
+      const int64_t s = x / f.chunk, j = x - s * f.chunk;
+      const int64_t n = std::min(f.x0 + f.len, (s + 1) * f.chunk) - x;
+      segs.push_back(Seg{static_cast<const uint16_t*>(shards[s]) + f.shard_off + j,
+                         f.dst + (x - f.x0), n});
+      x += n;
+    }
+  }
+}
+
+bool fan_pieces(const std::vector<Fan>& fans, int32_t world_n, std::vector<FanPiece>& pieces) {
+  pieces.clear();
+  if (world_n > kMaxFanRanks) return false;
+  for (const Fan& f : fans)
+    if (f.chunk > INT32_MAX) return false;
+  for (const Fan& f : fans) {
+    for (int64_t off = 0; off < f.len; off += kFanPiece) {
+      const int64_t x = f.x0 + off;
+      FanPiece p;
+      p.dst = f.dst + off;
+      p.shard_off = f.shard_off;
+      p.len = static_cast<int32_t>(std::min(kFanPiece, f.len - off));
+      p.chunk = static_cast<int32_t>(f.chunk);
+      p.s0 = static_cast<int32_t>(x / f.chunk);
+      p.j0 = static_cast<int32_t>(x % f.chunk);
+      p.first_chunk = 0;
+      p.vec = sbp::aligned(p.dst, 16) && f.shard_off % 8 == 0 && f.chunk % 8 == 0 && p.j0 % 8 == 0;
+      pieces.push_back(p);
+    }
+  }
+  return true;
+}
+
 
 }  // namespace sbp
 

@@ -1,5 +1,5 @@
 // Host fuzz driver for the copy-segment builders of the layout calls (pack,
-// unpack, shard_of, gather, unpack_shards), built with AddressSanitizer and
+// unpack, shard_of, gather, unpack_shards) and the fan pieces of the last two, built with AddressSanitizer and
 // UndefinedBehaviorSanitizer by tests/test_native_sanitize.py.  The GPU copy
 // kernel executes these segment lists as they are, so a segment outside its
 // buffers would be an out-of-bounds device write.  Here every list is
@@ -68,6 +68,42 @@ void run(const std::vector<sbp::Seg>& segs, std::vector<Buf*> dsts, std::vector<
     for (int64_t i = 0; i < s.len; ++i) {
       s.dst[i] = s.src ? s.src[i] : 0;
       written[d][s.dst + i - dsts[d]->p] += 1;
+    }
+  }
+  for (Buf* b : dsts) CHECK(b->guards_ok());
+}
+
+// Executes fan pieces element by element with the fan copy kernel's index
+// arithmetic (t = j0 + o in unsigned 32 bits, rank s0 + t / chunk, shard
+// position shard_off + t % chunk), checking that every read stays inside its
+// shard, every write inside a destination, and that a piece marked for
+// 16-byte copies keeps each group of 8 elements in one rank's chunk, aligned.
+void run_pieces(const std::vector<sbp::FanPiece>& pieces, const std::vector<const void*>& shards,
+                int64_t shard_numel, std::vector<Buf*> dsts, std::vector<std::vector<int>>& written) {
+  written.assign(dsts.size(), {});
+  for (size_t d = 0; d < dsts.size(); ++d) written[d].assign(dsts[d]->n, 0);
+  const int32_t N = static_cast<int32_t>(shards.size());
+  for (const sbp::FanPiece& f : pieces) {
+    CHECK(f.len >= 1 && f.len <= sbp::kFanPiece && f.chunk >= 1);
+    CHECK(f.s0 >= 0 && f.s0 < N && f.j0 >= 0 && f.j0 < f.chunk && f.first_chunk == 0);
+    CHECK(static_cast<uint64_t>(f.j0) + static_cast<uint64_t>(f.len) < (uint64_t{1} << 32));
+    int d = -1;
+    for (size_t k = 0; k < dsts.size(); ++k)
+      if (dsts[k]->holds(f.dst, f.len)) d = static_cast<int>(k);
+    CHECK(d >= 0);
+    if (f.vec) CHECK((reinterpret_cast<uintptr_t>(f.dst) & 15) == 0);
+    for (int64_t o = 0; o < f.len; ++o) {
+      const uint32_t t = static_cast<uint32_t>(f.j0) + static_cast<uint32_t>(o);
+      const uint32_t q = t / static_cast<uint32_t>(f.chunk);
+      const int64_t s = f.s0 + static_cast<int64_t>(q);
+      const int64_t pos = f.shard_off + (t - q * static_cast<uint32_t>(f.chunk));
+      CHECK(s < N && pos >= 0 && pos < shard_numel);
+      if (f.vec && o % 8 == 0 && o + 8 <= f.len) {
+        CHECK((t + 7) / static_cast<uint32_t>(f.chunk) == q);  // one rank's chunk
+        CHECK(pos % 8 == 0);                                    // 16-byte aligned read
+      }
+      f.dst[o] = static_cast<const uint16_t*>(shards[s])[pos];
+      written[d][f.dst + o - dsts[d]->p] += 1;
     }
   }
   for (Buf* b : dsts) CHECK(b->guards_ok());
@@ -192,6 +228,23 @@ void one_case(const Case& c) {
     CHECK(written[0][i] == (sel ? 1 : 0));
     CHECK(back.p[i] == (sel ? flat.p[i] : kSentinel));  // gather(shard_of(x)) = x
   }
+  {  // the same gather as fan pieces, the way the fan copy kernel reads them
+    std::vector<sbp::Fan> fans;
+    std::vector<sbp::FanPiece> pieces;
+    CHECK(sbp::gather_fans(p, bucket, shard_ptrs.data(), back.p, fans) == SBP_OK);
+    if (sbp::fan_pieces(fans, c.N, pieces)) {
+      CHECK(c.N <= sbp::kMaxFanRanks);
+      Buf via(F);
+      for (sbp::FanPiece& f : pieces) f.dst = via.p + (f.dst - back.p);
+      run_pieces(pieces, shard_ptrs, S, {&via}, written);
+      for (int64_t i = 0; i < F; ++i) {
+        CHECK(written[0][i] == ((i >= lo && i < hi) ? 1 : 0));
+        CHECK(via.p[i] == back.p[i]);
+      }
+    } else {
+      CHECK(c.N > sbp::kMaxFanRanks && pieces.empty());
+    }
+  }
   for (int32_t b = 0; b < nb; ++b) {  // shard s holds chunk s of each selected bucket
     int64_t chunk, so, fo;
     CHECK(sbp_plan_bucket(p, b, nullptr, nullptr, &chunk, &so, &fo) == SBP_OK);
@@ -227,6 +280,26 @@ void one_case(const Case& c) {
         CHECK(written[t][i] == (sel ? 1 : 0));
         CHECK(outs[t].p[i] == (sel ? ref.p[a + i] : kSentinel));
       }
+    }
+    // the same list as fan pieces, into fresh buffers, must give the same bits
+    std::vector<sbp::Fan> fans;
+    std::vector<sbp::FanPiece> pieces;
+    CHECK(sbp::unpack_shards_fans(p, bucket, shard_ptrs.data(), out_ptrs.data(), fans) == SBP_OK);
+    if (sbp::fan_pieces(fans, c.N, pieces)) {
+      std::vector<Buf> again;
+      std::vector<Buf*> again_bufs;
+      for (int32_t t = 0; t < T; ++t) again.emplace_back(c.numel[t]);
+      for (int32_t t = 0; t < T; ++t) again_bufs.push_back(&again[t]);
+      for (sbp::FanPiece& f : pieces) {
+        int32_t owner = -1;
+        for (int32_t t = 0; t < T; ++t)
+          if (outs[t].holds(f.dst, f.len)) owner = t;
+        CHECK(owner >= 0);
+        f.dst = again[owner].p + (f.dst - outs[owner].p);
+      }
+      run_pieces(pieces, shard_ptrs, S, again_bufs, written);
+      for (int32_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < c.numel[t]; ++i) CHECK(again[t].p[i] == outs[t].p[i]);
     }
   }
 
@@ -290,6 +363,31 @@ int main(int argc, char** argv) {
     CHECK(sbp::unpack_shards_segments(p, -1, shard_list, clash, segs) == SBP_EINVAL &&
           segs.empty());
     sbp_plan_free(p);
+  }
+  // long fans are cut into pieces of at most kFanPiece positions that resume
+  // where the one before stopped; a chunk beyond 32 bits, or more ranks than
+  // the kernel arguments hold, makes no pieces (nothing is executed here)
+  {
+    uint16_t* far = reinterpret_cast<uint16_t*>(uintptr_t{1} << 40);
+    const int64_t chunk = (int64_t{3} << 29) + 8, len = 5 * chunk + 100;
+    std::vector<sbp::Fan> fans = {sbp::Fan{64, chunk, 8, len, far}};
+    std::vector<sbp::FanPiece> pieces;
+    CHECK(sbp::fan_pieces(fans, 8, pieces));
+    int64_t off = 0;
+    for (const sbp::FanPiece& f : pieces) {
+      const int64_t x = 8 + off;
+      CHECK(f.dst == far + off && f.shard_off == 64 && f.chunk == chunk);
+      CHECK(f.s0 == x / chunk && f.j0 == x % chunk && f.len <= sbp::kFanPiece && f.len > 0);
+      CHECK(f.vec == 1 && static_cast<uint64_t>(f.j0) + f.len < (uint64_t{1} << 32));
+      off += f.len;
+    }
+    CHECK(off == len && pieces.size() == static_cast<size_t>((len + sbp::kFanPiece - 1) / sbp::kFanPiece));
+    CHECK(!sbp::fan_pieces(fans, sbp::kMaxFanRanks + 1, pieces) && pieces.empty());
+    fans[0].chunk = int64_t{1} << 31;
+    CHECK(!sbp::fan_pieces(fans, 8, pieces) && pieces.empty());
+    fans[0].chunk = 12;  // not a multiple of 8: element by element
+    fans[0].len = 30;
+    CHECK(sbp::fan_pieces(fans, 8, pieces) && pieces.size() == 1 && pieces[0].vec == 0);
   }
   printf("layout cases %d ok\n", iters);
   return 0;

@@ -443,9 +443,11 @@ def test_many_small_tensors(align):
 
 def test_layout_segment_longer_than_2_30():
     """A tensor of more than 2^30 elements: its copy segment is split into
-    pieces for the kernel (whose segment length is 32-bit).  Pack, unpack and
-    shard_of are checked at sampled positions around every piece boundary
-    and at random, against the generator's values recomputed on the host."""
+    pieces for the kernel (whose segment length is 32-bit), and so are the
+    fans of gather and unpack_shards.  Pack, unpack, shard_of, gather and
+    unpack_shards are checked at sampled positions around every piece and
+    rank-chunk boundary and at random, against the generator's values
+    recomputed on the host."""
     import torch
     big = (1 << 30) + 12345
     numels = [7, big, 3]
@@ -458,7 +460,11 @@ def test_layout_segment_longer_than_2_30():
     flat = torch.full((pl.flat_numel,), 0x3333, dtype=torch.int16, device=dev)
     sbp.pack_grads(pl, grads, flat)
     rng = np.random.default_rng(43)
-    edges = [0, 1, (1 << 30) - 1, 1 << 30, (1 << 30) + 1, big - 2, big - 1]
+    b1 = opl.buckets[opl.tensor_bucket[1]]
+    o1 = opl.tensor_flat_offset(1) - b1.flat_offset  # tensor 1's offset in its bucket
+    # piece cuts of segments and fans, and where rank 1's chunk starts
+    edges = [0, 1, (1 << 30) - 1, 1 << 30, (1 << 30) + 1, big - 2, big - 1,
+             (1 << 30) - o1 - 1, (1 << 30) - o1, b1.chunk - o1 - 1, b1.chunk - o1]
     idx = np.unique(np.r_[edges, rng.integers(0, big, 1 << 14)]).astype(np.int64)
     want = synth.normal_bf16_at(42, st[1], idx, 1e-2)
 
@@ -480,6 +486,7 @@ def test_layout_segment_longer_than_2_30():
     sbp.unpack_params(pl, flat, [None, out, out2], bucket=opl.tensor_bucket[1])
     H.assert_bits_equal(at(out, idx), want, "unpack of the big tensor")
     H.assert_bits_equal(H.to_np_u16(out2), synth.normal_bf16(42, st[2], 3, 1e-2), "unpack tensor 2")
+    shards = []
     for s in range(2):  # rank s's chunk of the big tensor's bucket
         shard = torch.empty(pl.shard_numel, dtype=torch.int16, device=dev)
         sbp.shard_of(pl, s, flat, shard)
@@ -487,6 +494,21 @@ def test_layout_segment_longer_than_2_30():
         j = np.unique(np.r_[0, b.chunk - 1, rng.integers(0, b.chunk, 4096)]).astype(np.int64)
         H.assert_bits_equal(at(shard, b.shard_offset + j), at(flat, b.flat_offset + s * b.chunk + j),
                             f"shard_of rank {s}")
+        shards.append(shard)
+    del out
+    back = torch.full((pl.flat_numel,), 0x2222, dtype=torch.int16, device=dev)
+    sbp.gather_shards(pl, shards, back, bucket=opl.tensor_bucket[1])
+    H.assert_bits_equal(at(back, off + idx), want, "gather of the big tensor's bucket")
+    H.assert_bits_equal(at(back, np.arange(b1.flat_offset, b1.flat_offset + b1.padded, 1 << 20)),
+                        at(flat, np.arange(b1.flat_offset, b1.flat_offset + b1.padded, 1 << 20)),
+                        "gather, every 2^20th position")
+    del back
+    out3 = torch.full((big,), 0x1111, dtype=torch.int16, device=dev)
+    out4 = torch.full((3,), 0x1111, dtype=torch.int16, device=dev)  # shares the bucket
+    sbp.unpack_shards(pl, shards, [None, out3, out4], bucket=opl.tensor_bucket[1])
+    H.assert_bits_equal(at(out3, idx), want, "unpack_shards of the big tensor")
+    H.assert_bits_equal(H.to_np_u16(out4), synth.normal_bf16(42, st[2], 3, 1e-2),
+                        "unpack_shards tensor 2")
     torch.cuda.synchronize()
 
 
@@ -572,8 +594,11 @@ def test_clipped_step_two_shards(max_norm):
 
 # ---- layout moves: pack / unpack / shard_of / gather on both plan kinds ---------
 
+# N = 64 is the most ranks gather and unpack_shards take as fans; at N = 80
+# they go out as plain segments
 @pytest.mark.parametrize("kind,N", [("whole", 4), ("split", 4), ("per_tensor", 4),
-                                    ("whole", 64), ("split", 64), ("per_tensor", 64)])
+                                    ("whole", 64), ("split", 64), ("per_tensor", 64),
+                                    ("whole", 80), ("per_tensor", 80)])
 @pytest.mark.parametrize("misalign", [False, True])
 def test_layout_moves(kind, N, misalign):
     import torch
