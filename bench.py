@@ -53,15 +53,16 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_adamw_llama3_8b_pmc.md")
 COPY_BYTES = 1 << 32  # the calibration copy moves 4 GiB in and 4 GiB out
 CALIBRATION_CALLS = 4  # --calibrate-copy: one warm-up copy + 3 timed ones
 KERNEL_SRC = os.path.join(ROOT, "sharded_bucket_plan_amd", "csrc", "shard_step.hip")
+LAYOUT_SRC = os.path.join(ROOT, "sharded_bucket_plan_amd", "csrc", "layout.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(path=KERNEL_SRC):
     h = hashlib.sha256()
-    with open(KERNEL_SRC, "rb") as f:
+    with open(path, "rb") as f:
         h.update(f.read())
     from sharded_bucket_plan_amd.build import FLAGS
     # the flags minus absolute paths (the tree lives elsewhere on other machines)
@@ -429,7 +430,9 @@ def summarize_pmc_kernels(base, command):
                 else f"{got_w / 1e9:.4f} / 0"
             lines.append(f"| {wl} | `{short}` | {len(F[k])} | {got_r / 1e9:.3f} / {alg_r / 1e9:.3f}"
                          f" = {got_r / alg_r:.4f} | {wcell} |")
-    lines += ["", f"source_sha256 (shard_step.hip and its build flags): {kernel_source_hash()}"]
+    lines += ["", f"source_sha256 (shard_step.hip and its build flags): {kernel_source_hash()}",
+              "", f"source_sha256 (layout.hip and its build flags): "
+              f"{kernel_source_hash(LAYOUT_SRC)}"]
     return "\n".join(lines) + "\n"
 
 

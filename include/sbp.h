@@ -330,6 +330,11 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers,
  * All device pointers 16-byte aligned and pairwise non-overlapping.
  * Errors: SBP_EINVAL, SBP_EALIGN, SBP_ERANGE (n > SBP_MAX_SHARD_NUMEL),
  * SBP_EHIP.
+ * Host cost: beta^t is formed by repeated float64 multiplication.  Each
+ * host thread keeps the powers of its last call and extends them when t
+ * grows, so consecutive steps cost one multiplication.  A call at a smaller
+ * t or with other betas starts again from 1, at up to min(t, 37.4 /
+ * -ln(beta)) multiplications per beta (past that 1 - beta^t is exactly 1).
  * ---------------------------------------------------------------------- */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;

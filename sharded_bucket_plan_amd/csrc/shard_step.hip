@@ -717,6 +717,15 @@ sbp_status dispatch_r(int32_t R, F&& f) {
 // belong to) and extended by the missing multiplications: the same sequence
 // of products, hence the same bits, at O(1) cost per step instead of O(t)
 // (about a millisecond at t = 10^6).  Any other call starts again from 1.
+//
+// The products need not run to t.  1 - x rounds to 1 in float64 for every
+// 0 <= x <= 2^-54 (at 2^-54 exactly, the tie goes to the even 1.0), and the
+// powers never grow (0 <= beta < 1), so once both are that small both
+// corrections are exactly 1 at this and every later step.  Waiting for them
+// to reach 0 instead would not end: a subnormal power can be a fixed point of
+// the rounded product (0.9 times 4 x 2^-1074 rounds back to 4 x 2^-1074).
+// Reaching 2^-54 takes about 37.4 / -ln(beta) products: 730 for 0.95, 37,400
+// for 0.999, and 6.3 x 10^8 (under a second) for the largest binary32 below 1.
 struct BetaPowers {
   float b1 = 0.0f, b2 = 0.0f;
   int64_t t = -1;  // no powers kept yet
@@ -736,9 +745,10 @@ void bias_corrections(const sbp_adamw_hparams& hp, double& bc1, double& bc2) {
     c.b2t = 1.0;
   }
   const double b1 = hp.beta1, b2 = hp.beta2;
+  constexpr double kOneMinusRoundsToOne = 0x1p-54;
   for (; c.t < hp.step; ++c.t) {
-    if (c.b1t == 0.0 && c.b2t == 0.0) {  // both powers have underflowed for good
-      c.t = hp.step;
+    if (c.b1t <= kOneMinusRoundsToOne && c.b2t <= kOneMinusRoundsToOne) {
+      c.t = hp.step;  // both corrections are 1 from here on
       break;
     }
     c.b1t *= b1;

@@ -953,7 +953,12 @@ def test_tensor_set_paths():
 def test_step_counts_in_any_order():
     """The bias corrections depend only on the step passed, whatever steps
     earlier calls used (forwards, backwards, repeated, far ahead, another
-    beta), each call checked against the oracle on fresh state."""
+    beta), each call checked against the oracle on fresh state.
+
+    Steps of 2^40 and 2^62 are beyond what the oracle's t multiplications
+    can reach; there both powers are far below 2^-54, where 1 - beta^t is
+    exactly 1, so the oracle's result at t = 10^6 (checked to have both
+    corrections exactly 1) is the result at those steps too."""
     import torch
     n, R = 256 * 8 * 2 + 7, 3
     th0, m0, v0 = _state(71, n)
@@ -962,13 +967,19 @@ def test_step_counts_in_any_order():
     peers_h = H.host_peers(71, 1, 0, R, n, 1e-3)
     peers_d = [H.from_np_u16(x) for x in peers_h]
     other = sbp.AdamW(1e-3, 0.8, 0.99, 1e-8, 0.01)
+    far = 10 ** 6
+    for hp in (HP, other):
+        sc_far = OS.adamw_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, far)
+        sc_one = OS.adamw_scalars(hp.lr, 0.0, 0.0, hp.eps, hp.weight_decay, 1)  # corrections 1
+        assert sc_far.step_size == sc_one.step_size and sc_far.c2 == sc_one.c2 == 1
     for t, hp in [(5, HP), (6, HP), (3, HP), (3, HP), (4, HP), (1000, HP), (7, HP),
-                  (7, other), (8, other), (2, HP), (10 ** 6, HP), (10 ** 6 + 1, HP), (1, HP)]:
+                  (7, other), (8, other), (2, HP), (10 ** 6, HP), (10 ** 6 + 1, HP), (1, HP),
+                  (1 << 40, HP), (1 << 62, other), ((1 << 62) + 1, other), (1 << 40, HP)]:
         dth, dm, dv = H.from_np_f32(th0), H.from_np_f32(m0), H.from_np_f32(v0)
         dp = H.empty_u16(n)
         sbp.adamw_shard(peers_d, None, 0.25, dth, dm, dv, dp, hp, t)
         torch.cuda.synchronize()
-        want = OS.shard_step(peers_h, None, np.float32(0.25), th0, m0, v0, hp, t)
+        want = OS.shard_step(peers_h, None, np.float32(0.25), th0, m0, v0, hp, min(t, far))
         got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
         worst = H.assert_state_close(got, want, f"step {t} betas {hp.beta1}/{hp.beta2}")
         assert worst == 0, f"step {t}: expected bit-exact, worst {worst} ulp"

@@ -617,3 +617,26 @@ def _check_shard_groups(numels, cap, tg):
             want = tg[owner[0]] if owner else prev
             assert g[j] == want
             prev = want
+
+
+def test_bias_corrections_settle_at_one():
+    """Facts of float64 arithmetic that let a caller stop forming beta^t early.
+    1 - x rounds to 1 exactly when 0 <= x <= 2^-54 (the tie at 2^-54 goes to
+    the even 1.0); a subnormal power can be a fixed point of the rounded
+    product, so waiting for 0 may never end; and once both powers are at most
+    2^-54 the oracle's scalars no longer change with t."""
+    tiny = 2.0 ** -54
+    assert 1.0 - tiny == 1.0
+    assert 1.0 - math.nextafter(tiny, 1.0) < 1.0
+    b = float(np.float32(0.9))
+    x = 4 * 2.0 ** -1074
+    assert x * b == x and x > 0.0
+    for beta1, beta2 in [(0.9, 0.95), (0.8, 0.99), (0.5, 0.5)]:
+        b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
+        t = 1
+        while b1 ** t > tiny or b2 ** t > tiny:
+            t += 1
+        base = S.adamw_scalars(1e-3, beta1, beta2, 1e-8, 0.1, t + 2)
+        for later in (t + 3, 2 * t + 50, 5 * t):
+            assert S.adamw_scalars(1e-3, beta1, beta2, 1e-8, 0.1, later) == base
+        assert base.c2 == 1.0 and base.step_size == np.float32(1e-3)
