@@ -56,6 +56,16 @@ class AdamWHParams(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("step", ctypes.c_int64)]
 
+    @classmethod
+    def of(cls, hp, step, what):
+        """The C struct of an AdamW and a step; a step outside int64 would
+        wrap silently in ctypes, so it is refused here (the library checks
+        step >= 1 itself)."""
+        step = int(step)
+        if not -(1 << 63) <= step < (1 << 63):
+            raise ValueError(f"{what}: step {step} does not fit int64")
+        return cls(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, step)
+
 
 class GroupHParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float)]
@@ -412,7 +422,7 @@ def adamw_shard(peers, acc, scale, master, m, v, param_out, hp, step, stream=Non
             raise ValueError(f"adamw_shard: {what} has the wrong size")
     if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
         raise ValueError("adamw_shard: peers/acc differ in size")
-    h = AdamWHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, int(step))
+    h = AdamWHParams.of(hp, step, "adamw_shard")
     _check(lib().sbp_adamw_shard(
         _ptrs(peers, "adamw_shard peers"), len(peers),
         None if acc is None else _f32(acc, "adamw_shard acc"), float(scale),
@@ -469,7 +479,7 @@ def adamw_shard_grouped(peers, acc, scale, master, m, v, param_out, hp, step, gr
         raise ValueError("adamw_shard_grouped: run tables differ in length")
     if not 1 <= len(groups) <= MAX_GROUPS:
         raise ValueError(f"adamw_shard_grouped: 1..{MAX_GROUPS} groups")
-    h = AdamWHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, int(step))
+    h = AdamWHParams.of(hp, step, "adamw_shard_grouped")
     gs = (GroupHParams * len(groups))(*[GroupHParams(lr, wd) for lr, wd in groups])
     _check(lib().sbp_adamw_shard_grouped(
         _ptrs(peers, "adamw_shard_grouped peers"), len(peers),

@@ -192,6 +192,24 @@ def test_device_calls_validate_before_launch():
     assert pack(plan.handle, -1, grads, V(0x100000 + 16), None) == sbp.SBP_EINVAL  # overlap
 
 
+def test_binding_refuses_steps_beyond_int64():
+    """ctypes would wrap a step of 2^64 + 5 to 5 without a word; the binding
+    refuses what does not fit the C struct's int64, and the library refuses
+    steps below 1."""
+    hp = sbp.AdamW()
+    assert sbp.AdamWHParams.of(hp, (1 << 63) - 1, "t").step == (1 << 63) - 1
+    for step in (1 << 63, (1 << 64) + 5, -(1 << 63) - 1):
+        with pytest.raises(ValueError, match="does not fit int64"):
+            sbp.AdamWHParams.of(hp, step, "t")
+    V = ctypes.c_void_p
+    peers = (V * 1)(0x100000)
+    for step in (0, -1, -(1 << 63)):
+        h = sbp.AdamWHParams.of(hp, step, "t")
+        assert sbp.lib().sbp_adamw_shard(peers, 1, None, 1.0, V(0x300000), V(0x400000),
+                                         V(0x500000), V(0x600000), 16, ctypes.byref(h),
+                                         None) == sbp.SBP_EINVAL
+
+
 def test_clip_scale_matches_oracle():
     import math
     from oracle import step as OS
