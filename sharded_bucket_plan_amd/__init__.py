@@ -505,6 +505,8 @@ def grad_sq_norm(peers, acc, scale, n, g_sum_out=None, workspace=None, sq_out=No
     """
     import torch
     ref = peers[0] if peers else acc
+    if ref is None:
+        raise ValueError("grad_sq_norm: needs peers or an accumulator")
     dev = ref.device
     if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
         raise ValueError("grad_sq_norm: peers/acc differ in size")

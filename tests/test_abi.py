@@ -210,6 +210,11 @@ def test_binding_refuses_steps_beyond_int64():
                                          None) == sbp.SBP_EINVAL
 
 
+def test_grad_sq_norm_needs_an_input():
+    with pytest.raises(ValueError, match="needs peers or an accumulator"):
+        sbp.grad_sq_norm([], None, 1.0, 0)
+
+
 def test_clip_scale_matches_oracle():
     import math
     from oracle import step as OS
