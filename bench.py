@@ -352,6 +352,10 @@ PMC_KERNEL_RUNS = (
     ("dp", "llama3_8b_dp", "--workload llama3_8b_dp --steps 2 --warmup 1"),
     ("clip", "llama3_8b", "--clip 1.0 --steps 3 --warmup 1"),
     ("b7", "gpt_7b5", "--workload gpt_7b5 --steps 3 --warmup 1"),
+    ("gather", "llama3_8b", "--layout-call gather_shards --steps 3 --warmup 1"),
+    ("ushards", "llama3_8b", "--layout-call unpack_shards --steps 3 --warmup 1"),
+    ("gather_pt", "gpt2_small",
+     "--layout-call gather_shards --plan per_tensor --workload gpt2_small --steps 3 --warmup 1"),
 )
 
 
@@ -396,7 +400,8 @@ def summarize_pmc_kernels(base, command):
              f"Calibration (4 GiB copies, {CALIBRATION_CALLS} calls): bytes read = 1024 x "
              f"FETCH_SIZE x {fs:.4f}, bytes written = 1024 x WRITE_SIZE x {ws:.4f}.  "
              "Per step: the kernel's dispatches "
-             "summed over the run, divided by its steps (warm-up included).  The squared-norm "
+             "summed over the run, divided by its steps (warm-up included); a step of a "
+             "--layout-call run is one call of that layout call.  The squared-norm "
              "pass also writes one 8-byte partial per 2048-element tile, which its algorithmic "
              "bytes leave out.", "",
              "| workload | kernel | dispatches | read GB counted / algorithmic | "
@@ -410,22 +415,33 @@ def summarize_pmc_kernels(base, command):
             F.setdefault(k, []).append(x)
         for k, x in _pmc_rows(os.path.join(base, f"{run}_WRITE_SIZE"), "WRITE_SIZE"):
             W.setdefault(k, []).append(x)
+        call = flags.split("--layout-call ")[1].split()[0] if "--layout-call" in flags else None
+        if call:  # one layout call per step: its bytes from the plan
+            kind = flags.split("--plan ")[1].split()[0] if "--plan " in flags else "whole"
+            pl = layout_plan(w, kind)
+            call_bytes = LAYOUT_CALL_BYTES[call](sum(w.numels), pl.flat_numel, pl.shard_numel)
         for k in sorted(F):
-            if "copy_kernel" in k:
-                rd, wr, short = 2, 2, "copy_kernel (pack)"
+            if call:
+                if "copy_kernel" not in k:
+                    continue
+                base_name = "fan_copy_kernel" if "fan_copy_kernel" in k else "copy_kernel"
+                short = f"{base_name} ({call}, {kind} plan)"
+                alg_r, alg_w = call_bytes
+            elif "copy_kernel" in k:
+                # a pack covers the flat buffer once per step, in however many launches
+                short = "copy_kernel (pack)"
+                alg_r, alg_w = 2 * n, 2 * n
             else:
                 rw = _kernel_read_write(k, w.R)
                 if rw is None:
                     continue
-                rd, wr = rw
                 short = k.split("(anonymous namespace)::")[1].split("(")[0] if \
                     "(anonymous namespace)::" in k else k
+                launches = len(F[k]) / steps
+                alg_r, alg_w = rw[0] * n * launches, rw[1] * n * launches
             per = 1.0 / steps
             got_r = sum(F[k]) * 1024 * fs * per
             got_w = sum(W.get(k, [0.0])) * 1024 * ws * per
-            # a pack covers the flat buffer once per step, in however many launches
-            launches = 1 if "copy_kernel" in k else len(F[k]) / steps
-            alg_r, alg_w = rd * n * launches, wr * n * launches
             wcell = f"{got_w / 1e9:.3f} / {alg_w / 1e9:.3f} = {got_w / alg_w:.4f}" if alg_w \
                 else f"{got_w / 1e9:.4f} / 0"
             lines.append(f"| {wl} | `{short}` | {len(F[k])} | {got_r / 1e9:.3f} / {alg_r / 1e9:.3f}"
@@ -554,6 +570,78 @@ def bucket_sweep(seed, reps=5):
     return {"bucket_sweep": rows, "fit": fit, "bytes_per_pass": M, "shard_numel": n}
 
 
+def layout_plan(w, plan_kind):
+    """The plan of a workload's model under one plan kind (whole, split or
+    per_tensor)."""
+    import sharded_bucket_plan_amd as sbp
+    if plan_kind == "split":
+        return sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n, split=True)
+    if plan_kind == "per_tensor":
+        rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
+        return sbp.bucket_plan_per_tensor(w.numels, w.world_n, rows)
+    return sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+
+
+# Algorithmic bytes of one layout call (read, written), from the plan:
+# per-tensor element counts P, flat (padded) numel F, shard numel n.
+LAYOUT_CALL_BYTES = {
+    "pack_grads": lambda P, F, n: (2 * P, 2 * F),
+    "shard_of": lambda P, F, n: (2 * n, 2 * n),
+    "gather_shards": lambda P, F, n: (2 * F, 2 * F),
+    "unpack_params": lambda P, F, n: (2 * P, 2 * P),
+    "unpack_shards": lambda P, F, n: (2 * P, 2 * P),
+}
+
+
+def layout_call(seed, workload, plan_kind, call, warmup, steps):
+    """One layout call made eagerly warmup + steps times on a workload's model,
+    nothing else launched on the GPU after the inputs are generated: the run a
+    counter pass divides by its number of calls.  Returns the calls made and
+    the median time of the timed ones (HIP events on the launch stream)."""
+    import statistics as st
+    import torch
+    import sharded_bucket_plan_amd as sbp
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    pl = layout_plan(w, plan_kind)
+    n, F, P = pl.shard_numel, pl.flat_numel, sum(w.numels)
+    flat = torch.empty(F, dtype=torch.int16, device=dev)
+    shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
+                                    synth.peer_stream(1, 0, r), w.grad_sigma)
+              for r in range(w.world_n)]
+    tensors = [torch.empty(k, dtype=torch.int16, device=dev) for k in w.numels]
+    for t, x in enumerate(tensors):
+        synth.dev_normal_bf16(x, seed, synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
+    tset = sbp.TensorSet(pl, tensors)
+    run = {
+        "pack_grads": lambda: sbp.pack_grads(pl, tset, flat),
+        "shard_of": lambda: sbp.shard_of(pl, 0, flat, shards[0]),
+        "gather_shards": lambda: sbp.gather_shards(pl, shards, flat),
+        "unpack_params": lambda: sbp.unpack_params(pl, flat, tset),
+        "unpack_shards": lambda: sbp.unpack_shards(pl, shards, tset),
+    }[call]
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    rd, wr = LAYOUT_CALL_BYTES[call](P, F, n)
+    med = st.median(ms)
+    log(f"layout call: {call} ({plan_kind}, {workload}) x {warmup + steps}, {med:.3f} ms median")
+    return {"call": call, "plan": plan_kind, "workload": workload, "calls": warmup + steps,
+            "ms_median": med, "algorithmic_bytes": rd + wr,
+            "gbs": (rd + wr) / (med * 1e-3) / 1e9}
+
+
 def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     """The layout calls on a workload's model (default Llama-3-8B at N = 8:
     162 buckets of 291 tensors, 8,030,261,248 elements) under one plan kind
@@ -578,12 +666,7 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     w = synth.WORKLOADS[workload]
     dev = torch.device("cuda:0")
     rows = [s[1] if len(s) == 2 else 1 for _, s in w.params]
-    if plan_kind == "split":
-        pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n, split=True)
-    elif plan_kind == "per_tensor":
-        pl = sbp.bucket_plan_per_tensor(w.numels, w.world_n, rows)
-    else:
-        pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
+    pl = layout_plan(w, plan_kind)
     n, F, P = pl.shard_numel, pl.flat_numel, sum(w.numels)
     flat = torch.empty(F, dtype=torch.int16, device=dev)
     shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
@@ -780,6 +863,9 @@ def main():
     ap.add_argument("--plan", choices=["whole", "split", "per_tensor"], default="whole",
                     help="with --layout: the plan whose layout is timed (whole-tensor buckets, "
                          "fixed-size split buckets, or one bucket per tensor with row shards)")
+    ap.add_argument("--layout-call", choices=sorted(LAYOUT_CALL_BYTES),
+                    help="only make this layout call --warmup + --steps times, eagerly, on "
+                         "--workload's model under --plan (a counter pass of one kernel)")
     ap.add_argument("--stream-mix", action="store_true",
                     help="only time the library's kernels against their read/write stream mix "
                          "on the Llama-3-8B shard and print their JSON")
@@ -817,6 +903,10 @@ def main():
         return
     if args.layout:
         print(json.dumps(layout_moves(seed, args.workload, args.plan)), flush=True)
+        return
+    if args.layout_call:
+        print(json.dumps(layout_call(seed, args.workload, args.plan, args.layout_call,
+                                     args.warmup, args.steps)), flush=True)
         return
     if args.stream_mix:
         print(json.dumps(stream_mix(seed)), flush=True)
