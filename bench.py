@@ -463,20 +463,22 @@ def host_cpu_model():
     return None
 
 
-def cpu_baseline(workload_name, seed, target_s):
-    """The oracle as it stands, on a bounded contiguous sample of the same
-    workload's shard (inputs generated on the host), single-threaded numpy."""
+def _oracle_slices(workload_name, seed, first, stride, target_s, chunk=1 << 22):
+    """Runs the oracle's fused step over contiguous slices of `chunk` elements
+    of the workload's shard (slices first, first + stride, ...; inputs
+    generated on the host, outside the timing) until `target_s` seconds of
+    oracle work.  Returns (elements done, seconds spent in the oracle)."""
     import numpy as np
     import synth
     from oracle import step as OS
 
     w = synth.WORKLOADS[workload_name]
     hp = w.adamw
-    chunk = 1 << 22
     done = 0
     spent = 0.0
-    i0 = 0
+    k = first
     while spent < target_s:
+        i0 = k * chunk
         peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), chunk, w.grad_sigma, i0)
                  for r in range(w.R)]
         th = synth.normal_f32(seed, synth.master_stream(0), chunk, w.master_sigma, i0)
@@ -487,7 +489,18 @@ def cpu_baseline(workload_name, seed, target_s):
         OS.shard_step(peers, acc, scale, th, z, z, hp, 1)
         spent += time.perf_counter() - t0
         done += chunk
-        i0 += chunk
+        k += stride
+    return done, spent
+
+
+def cpu_baseline(workload_name, seed, target_s):
+    """The oracle as it stands, on a bounded contiguous sample of the same
+    workload's shard (inputs generated on the host), single-threaded numpy."""
+    import synth
+
+    w = synth.WORKLOADS[workload_name]
+    chunk = 1 << 22
+    done, spent = _oracle_slices(workload_name, seed, 0, 1, target_s, chunk)
     b = fused_bytes_per_elem(w.R, w.K > 1)
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
             "gbs": done * b / spent / 1e9, "host_cpu": host_cpu_model(),
@@ -496,6 +509,68 @@ def cpu_baseline(workload_name, seed, target_s):
                        f"{workload_name} shard, one fused step (R={w.R}"
                        f"{', with accumulator' if w.K > 1 else ''}), numpy binary32 oracle, "
                        f"{spent:.1f} s")}
+
+
+def _oracle_core_worker(workload_name, seed, k, target_s, chunk, barrier, results):
+    """One core's share of cpu_oracle_cores: slice k of the shard generated
+    first, then, from the common start, the oracle's fused step on it over
+    and over for `target_s` seconds (its time does not depend on the values)."""
+    import numpy as np
+    import synth
+    from oracle import step as OS
+
+    w = synth.WORKLOADS[workload_name]
+    i0 = k * chunk
+    peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), chunk, w.grad_sigma, i0)
+             for r in range(w.R)]
+    th = synth.normal_f32(seed, synth.master_stream(0), chunk, w.master_sigma, i0)
+    z = np.zeros(chunk, np.float32)
+    acc = OS.reduce_peers(peers) if w.K > 1 else None
+    scale = OS.mean_scale(w.R, w.K)
+    barrier.wait()
+    t0 = time.perf_counter()
+    done = 0
+    while time.perf_counter() - t0 < target_s:
+        OS.shard_step(peers, acc, scale, th, z, z, w.adamw, 1)
+        done += chunk
+    results.put((k, done, time.perf_counter() - t0))
+
+
+def cpu_oracle_cores(workload_name, seed, procs, target_s):
+    """The same oracle on `procs` host cores at once: one worker process per
+    core, each on its own slice of the shard (the step is elementwise, so the
+    slices are independent).  Inputs are generated before a common start;
+    after it each worker runs only the oracle, for about `target_s` seconds.
+    Throughput is all elements done over the longest worker's time.  The
+    worker processes are started from a process that never touches the GPU."""
+    import multiprocessing as mp
+    import synth
+
+    w = synth.WORKLOADS[workload_name]
+    chunk = 1 << 22
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(procs)
+    results = ctx.Queue()
+    workers = [ctx.Process(target=_oracle_core_worker,
+                           args=(workload_name, seed, k, target_s, chunk, barrier, results))
+               for k in range(procs)]
+    for p in workers:
+        p.start()
+    res = [results.get(timeout=600) for _ in range(procs)]
+    for p in workers:
+        p.join()
+    if any(p.exitcode != 0 for p in workers):
+        raise RuntimeError("cpu_oracle_cores: a worker failed")
+    done = sum(d for _, d, _ in res)
+    wall = max(t for _, _, t in res)
+    b = fused_bytes_per_elem(w.R, w.K > 1)
+    return {"value": done / wall, "unit": "params/s", "cores": procs, "kind": "oracle",
+            "gbs": done * b / wall / 1e9, "wall_s": wall,
+            "per_core_params_per_s": [d / t for _, d, t in sorted(res)],
+            "host_cpu": host_cpu_model(), "host_threads_available": os.cpu_count(),
+            "sample": (f"{procs} slices of {chunk} elements of the {workload_name} shard, one "
+                       f"per worker process, each stepped repeatedly for {target_s:.0f} s "
+                       f"(one fused step, R={w.R}), numpy binary32 oracle")}
 
 
 def bucket_sweep(seed, reps=5):
@@ -848,6 +923,10 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-oracle-cores", type=int, metavar="P",
+                    help="only time the oracle on P host cores at once (about --cpu-seconds "
+                         "of oracle work per core, --workload's shard) and print its JSON; "
+                         "the GPU is not used")
     ap.add_argument("--clip", type=float, default=None, metavar="MAX_NORM",
                     help="add global gradient-norm clipping to the step")
     ap.add_argument("--groups", action="store_true",
@@ -886,6 +965,12 @@ def main():
         print(summarize_pmc_kernels(*args.summarize_pmc_kernels), end="")
         return
 
+    if args.cpu_oracle_cores:
+        import synth
+        seed = synth.SEED if args.seed is None else args.seed
+        print(json.dumps(cpu_oracle_cores(args.workload, seed, args.cpu_oracle_cores,
+                                          args.cpu_seconds)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "shard step is per rank and nothing here crosses GPUs", file=sys.stderr)
