@@ -416,7 +416,8 @@ def test_pack_big_tensors_many_launches():
 def test_many_small_tensors(align):
     """5,000 small tensors (0-300 elements) at N = 8: thousands of copy
     segments, so many launches filled up to 160 small segments each; pack,
-    then the shards straight into per-tensor buffers, against the oracle."""
+    then the shards straight into per-tensor buffers and back into the flat
+    buckets, against the oracle."""
     import torch
     rng = np.random.default_rng(align)
     numels = [int(x) for x in rng.integers(0, 301, 5000)]
@@ -434,8 +435,12 @@ def test_many_small_tensors(align):
         sbp.shard_of(pl, s, flat, shards[s])
     outs = [H.empty_u16(k) for k in numels]
     sbp.unpack_shards(pl, shards, outs)
+    back = H.empty_u16(pl.flat_numel)
+    back.fill_(0x1234)
+    sbp.gather_shards(pl, shards, back)  # with align = 1, chunks that are not multiples of 8
     torch.cuda.synchronize()
     H.assert_bits_equal(H.to_np_u16(flat), want, "pack of 5,000 tensors")
+    H.assert_bits_equal(H.to_np_u16(back), want, "gather_shards of 5,000 tensors")
     for t, h in enumerate(gh):
         if h.size:
             H.assert_bits_equal(H.to_np_u16(outs[t]), h, f"unpack_shards tensor {t}")
