@@ -11,9 +11,13 @@
 //
 // Design.  Every kernel here is a single pass over HBM with no reuse, so it
 // is bandwidth-bound (about 0.5 flop per byte against a ridge near 20):
-//   - each lane owns 8 consecutive elements: one 16-byte load per bf16 peer,
-//     two 16-byte loads per fp32 stream, 16-byte stores; all loads of a lane
-//     are issued before any arithmetic;
+//   - each lane owns 8 elements of its tile, and issues all its loads before
+//     any arithmetic.  Mostly they are 8 consecutive elements: one 16-byte
+//     load per bf16 peer, two 16-byte loads per fp32 stream, 16-byte stores.
+//     The fused step with at most 2 peers splits them into two runs of 4, a
+//     wave's 64 lanes covering 256 consecutive elements with each run (each
+//     fp32 instruction of the wave one contiguous kilobyte; see
+//     fused_split_tile);
 //   - R is a template parameter so the peer loop unrolls and the peer
 //     pointers stay in scalar registers (passed by value in the kernel
 //     arguments);
@@ -323,9 +327,10 @@ accumulate_kernel(Peers P, float* __restrict__ acc, int64_t n) {
 // 1.0B shard, round-robin in two processes against 8 consecutive elements
 // per lane: R = 2 +1.0 / +2.1 points of 8 TB/s, the update from G (R = 0)
 // +0.9 / +1.4.  With R = 8 the same map needs twice the peer load
-// instructions and measured 0.5 points slower; moving the peer sums through
-// LDS instead (16-byte peer loads) gained under 0.4 points, so R >= 3 keeps
-// 8 consecutive elements per lane.
+// instructions and measured 0.5 points slower; loading each peer's 8
+// elements with one 16-byte load and swapping halves between the two lanes
+// of a pair with a lane shuffle measured -0.55 points (+0.15 with the
+// accumulator), so R >= 3 keeps 8 consecutive elements per lane.
 __device__ __forceinline__ void bf16x4(u32x2 u, float (&x)[4]) {
   x[0] = bf16_lo(u.x);
   x[1] = bf16_hi(u.x);
@@ -725,7 +730,8 @@ sbp_status dispatch_r(int32_t R, F&& f) {
 // to reach 0 instead would not end: a subnormal power can be a fixed point of
 // the rounded product (0.9 times 4 x 2^-1074 rounds back to 4 x 2^-1074).
 // Reaching 2^-54 takes about 37.4 / -ln(beta) products: 730 for 0.95, 37,400
-// for 0.999, and 6.3 x 10^8 (under a second) for the largest binary32 below 1.
+// for 0.999, and 6.3 x 10^8 (of the order of a second) for the largest
+// binary32 below 1.
 struct BetaPowers {
   float b1 = 0.0f, b2 = 0.0f;
   int64_t t = -1;  // no powers kept yet
