@@ -1,7 +1,8 @@
-// Host side of the layout calls: validation, and the copy-segment lists the
-// copy kernel executes (layout.hip).  Pure host code, so it also builds with
-// g++ for the sanitizer tests; the kernel trusts these lists, so every
-// segment must lie inside the buffers it names.
+// Host side of the layout calls: validation, the copy-segment lists the copy
+// kernel executes, and the fan lists (with their kernel-argument pieces) of
+// the calls that read across the N shards (layout.hip).  Pure host code, so
+// it also builds with g++ for the sanitizer tests; the kernels trust these
+// lists, so every segment and every fan must lie inside the buffers it names.
 //
 // Segments follow the plan ("Parallelisms", Gradient bucketing: gradients at
 // fixed offsets in flat buffers; FSDP / Flat parameter: the originals are
