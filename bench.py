@@ -142,6 +142,9 @@ class Workload:
             s["peers"] = s["mb"][-1]
         if self.acc:
             s["acc"] = self._f32(n)
+        # the plain step's buffers marshalled once (the step the timed loop makes)
+        s["step"] = self.sbp.ShardStep(s["peers"], s.get("acc"), s["master"], s["m"], s["v"],
+                                       s["p"])
         if self.clip:
             s["gsum"] = self._f32(n)
             s["ws"] = self.torch.empty(self.sbp.grad_sq_norm_workspace(n),
@@ -205,8 +208,7 @@ class Workload:
             sbp.adamw_shard_grouped(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"],
                                     s["p"], self.hp, t, self.groups, *self.runs)
         else:
-            sbp.adamw_shard(s["peers"], s.get("acc"), scale, s["master"], s["m"], s["v"],
-                            s["p"], self.hp, t)
+            s["step"](scale, self.hp, t)
         mark("fused_adamw_kernel", 1)
 
     def config(self):

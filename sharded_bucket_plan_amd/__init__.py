@@ -431,6 +431,43 @@ def adamw_shard(peers, acc, scale, master, m, v, param_out, hp, step, stream=Non
         _stream(stream, master)))
 
 
+class ShardStep:
+    """sbp_adamw_shard with its buffers marshalled once.
+
+    A training loop steps the same shard buffers every iteration.  Building
+    the peer pointer array, checking sizes and dtypes and looking up the
+    stream once leaves each call with the hyperparameter struct and the C
+    call, which is what a small shard's step rate is bound by.  The launch
+    stream is the one given, else the current stream at construction.  The
+    object holds references to its tensors.
+
+        step = sbp.ShardStep(peers, acc, master, m, v, param_out)
+        step(scale, hp, t)   # = adamw_shard(peers, acc, scale, ..., hp, t)
+    """
+
+    def __init__(self, peers, acc, master, m, v, param_out, stream=None):
+        n = master.numel()
+        for t, what in ((m, "m"), (v, "v"), (param_out, "param_out")):
+            if t.numel() != n:
+                raise ValueError(f"ShardStep: {what} has the wrong size")
+        if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
+            raise ValueError("ShardStep: peers/acc differ in size")
+        self.tensors = (list(peers), acc, master, m, v, param_out)
+        self.n = n
+        self.R = len(peers)
+        self._args = (_ptrs(peers, "ShardStep peers"), self.R,
+                      None if acc is None else _f32(acc, "ShardStep acc"))
+        self._state = (_f32(master, "ShardStep master"), _f32(m, "ShardStep m"),
+                       _f32(v, "ShardStep v"), _dev(param_out, 2, "ShardStep param_out"), n)
+        self._stream = _stream(stream, master)
+
+    def __call__(self, scale, hp, step):
+        h = AdamWHParams.of(hp, step, "ShardStep")
+        peers, R, acc = self._args
+        _check(lib().sbp_adamw_shard(peers, R, acc, float(scale), *self._state, ctypes.byref(h),
+                                     self._stream))
+
+
 def group_runs(plan, rank, tensor_group):
     """sbp_group_runs: rank's shard as runs of one parameter group.
 

@@ -988,3 +988,33 @@ def test_step_counts_in_any_order():
         got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
         worst = H.assert_state_close(got, want, f"step {t} betas {hp.beta1}/{hp.beta2}")
         assert worst == 0, f"step {t}: expected bit-exact, worst {worst} ulp"
+
+
+def test_shard_step_object_matches_the_call():
+    """ShardStep (buffers marshalled once) makes the same C call as
+    adamw_shard: three steps each way, with and without an accumulator,
+    bit-identical, and against the oracle."""
+    import torch
+    n, R = 256 * 8 * 3 + 5, 3
+    peers_h = H.host_peers(81, 1, 0, R, n, 1e-3)
+    acc_h = np.asarray(OS.reduce_peers(H.host_peers(81, 1, 1, 2, n, 1e-3)), np.float32)
+    th0, m0, v0 = _state(82, n)
+    for with_acc in (False, True):
+        peers = [H.from_np_u16(x) for x in peers_h]
+        acc = H.from_np_f32(acc_h) if with_acc else None
+        a = [H.from_np_f32(x) for x in (th0, m0, v0)] + [H.empty_u16(n)]
+        b = [H.from_np_f32(x) for x in (th0, m0, v0)] + [H.empty_u16(n)]
+        step = sbp.ShardStep(peers, acc, *b)
+        want = (th0, m0, v0, None)
+        for t in (1, 2, 3):
+            sbp.adamw_shard(peers, acc, 0.25, *a, HP, t)
+            step(0.25, HP, t)
+            want = OS.shard_step(peers_h, acc_h if with_acc else None, np.float32(0.25),
+                                 want[0], want[1], want[2], HP, t)
+        torch.cuda.synchronize()
+        for x, y, what in zip(a, b, ("master", "m", "v", "param")):
+            assert torch.equal(x, y), f"ShardStep {what} differs (acc={with_acc})"
+        got = (H.to_np_f32(b[0]), H.to_np_f32(b[1]), H.to_np_f32(b[2]), H.to_np_u16(b[3]))
+        assert H.assert_state_close(got, want, f"ShardStep acc={with_acc}") == 0
+    with pytest.raises(ValueError, match="wrong size"):
+        sbp.ShardStep(peers, None, a[0], a[1][:-1], a[2], a[3])
