@@ -38,6 +38,10 @@
  *     call only.
  *   - Device calls validate on the host, enqueue on `stream` and return;
  *     a fault in a kernel surfaces at the caller's next synchronisation.
+ *   - Before it launches, a device call reads and clears the calling
+ *     thread's last HIP error (hipGetLastError), so that SBP_EHIP reports a
+ *     launch of its own.  A caller that checks hipGetLastError for its own
+ *     earlier launches does so before calling into the library.
  *   - bf16 values are passed as their 16-bit patterns (uint16 storage).
  *   - Arithmetic is IEEE binary32 with one round-to-nearest-even rounding per
  *     operation (no fused multiply-add), subnormals kept; a sum over peers
