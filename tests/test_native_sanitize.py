@@ -43,4 +43,4 @@ def test_planner_under_asan_ubsan(tmp_path):
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
 def test_layout_segments_under_asan_ubsan(tmp_path):
-    _build_and_run(tmp_path, "layout_fuzz", ["layout_host.cpp", "plan.cpp"], 4000, "ok")
+    _build_and_run(tmp_path, "layout_fuzz", ["layout_host.cpp", "plan.cpp"], 12000, "ok")
