@@ -1016,5 +1016,16 @@ def test_shard_step_object_matches_the_call():
             assert torch.equal(x, y), f"ShardStep {what} differs (acc={with_acc})"
         got = (H.to_np_f32(b[0]), H.to_np_f32(b[1]), H.to_np_f32(b[2]), H.to_np_u16(b[3]))
         assert H.assert_state_close(got, want, f"ShardStep acc={with_acc}") == 0
+    # a stream given at construction is the one every call launches on
+    side = torch.cuda.Stream()
+    c = [H.from_np_f32(x) for x in (th0, m0, v0)] + [H.empty_u16(n)]
+    torch.cuda.synchronize()
+    on_side = sbp.ShardStep(peers, acc, *c, stream=side)
+    assert on_side._stream.value == side.cuda_stream
+    for t in (1, 2, 3):
+        on_side(0.25, HP, t)
+    side.synchronize()
+    for x, y, what in zip(c, b, ("master", "m", "v", "param")):
+        assert torch.equal(x, y), f"ShardStep on a side stream: {what} differs"
     with pytest.raises(ValueError, match="wrong size"):
         sbp.ShardStep(peers, None, a[0], a[1][:-1], a[2], a[3])
