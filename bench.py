@@ -19,7 +19,9 @@ HBM:
 value = shard elements updated per second (whole job = the one GPU).
 
 Variants of the step (same JSON line): --clip MAX_NORM adds global-norm
-clipping (the norm pass writing G, then the update from G); --groups uses
+clipping (the norm pass writing G, then the update from G; with
+--clip-recompute the norm pass writes nothing and the update sums the peers
+again); --groups uses
 two parameter groups (no weight decay on 1-D tensors) and the grouped step.
 Other modes print their own JSON: --layout times pack / shard_of /
 gather_shards / unpack_params / unpack_shards and the plan builds on the workload's model
@@ -77,7 +79,7 @@ def fused_bytes_per_elem(R, acc):
 class Workload:
     """Device buffers and the per-step launches of one workload."""
 
-    def __init__(self, name, seed, clip=None, groups=False):
+    def __init__(self, name, seed, clip=None, groups=False, recompute=False):
         import torch
         import sharded_bucket_plan_amd as sbp
         import synth
@@ -93,6 +95,8 @@ class Workload:
         self.n = self.plan.shard_numel
         self.acc = w.K > 1
         self.clip = clip
+        # clipping without G: the norm pass only reads, the update reads the peers again
+        self.recompute = bool(clip) and recompute
         self.groups = None
         if groups:
             # the usual two parameter groups: decay on matrices, none on 1-D
@@ -101,7 +105,7 @@ class Workload:
             self.groups = [(self.hp.lr, self.hp.weight_decay), (self.hp.lr, 0.0)]
             self.runs = sbp.group_table(self.plan, w.shard_index, tg, self.dev)
         # with clipping the update reads G (fp32) written by the norm pass
-        self.bytes_fused = (fused_bytes_per_elem(0, True) if clip else
+        self.bytes_fused = (fused_bytes_per_elem(0, True) if clip and not self.recompute else
                             fused_bytes_per_elem(w.R, self.acc)) * self.n
         mall = 256 << 20
         set_bytes = self.bytes_fused
@@ -167,7 +171,8 @@ class Workload:
         if self.acc:
             out.append(("accumulate_kernel", (2 * w.R + 4) * n + (2 * w.R + 8) * n * (w.K - 2)))
         if self.clip:
-            out.append(("sq_norm_kernel", (2 * w.R + (4 if self.acc else 0) + 4) * n))
+            out.append(("sq_norm_kernel", (2 * w.R + (4 if self.acc else 0)
+                                           + (0 if self.recompute else 4)) * n))
         out.append(("fused_adamw_kernel", self.bytes_fused))
         return out
 
@@ -195,12 +200,17 @@ class Workload:
         if self.clip:
             # this rank's squared norm; with more ranks its all-reduce goes here
             mark("sq_norm_kernel", 0)
-            sbp.grad_sq_norm(s["peers"], s.get("acc"), scale, self.n, g_sum_out=s["gsum"],
+            sbp.grad_sq_norm(s["peers"], s.get("acc"), scale, self.n,
+                             g_sum_out=None if self.recompute else s["gsum"],
                              workspace=s["ws"], sq_out=s["sq"])
             mark("sq_norm_kernel", 1)
             scale, _ = sbp.clip_scale(s["sq"].item(), self.clip, scale)
             mark("fused_adamw_kernel", 0)
-            sbp.adamw_shard([], s["gsum"], scale, s["master"], s["m"], s["v"], s["p"], self.hp, t)
+            if self.recompute:
+                s["step"](scale, self.hp, t)
+            else:
+                sbp.adamw_shard([], s["gsum"], scale, s["master"], s["m"], s["v"], s["p"],
+                                self.hp, t)
             mark("fused_adamw_kernel", 1)
             return
         mark("fused_adamw_kernel", 0)
@@ -218,6 +228,7 @@ class Workload:
                 "bucket_cap_MiB": w.bucket_cap_bytes >> 20, "buckets": self.plan.num_buckets,
                 "pack": w.pack, "rotating_buffer_sets": self.nsets,
                 "clip_max_norm": self.clip,
+                "clip_recompute": self.recompute,
                 "param_groups": len(self.groups) if self.groups else 1,
                 "group_runs": int(self.runs[0].numel()) if self.groups else 1,
                 "fused_bytes_per_elem": self.bytes_fused // self.n}
@@ -931,6 +942,9 @@ def main():
                          "the GPU is not used")
     ap.add_argument("--clip", type=float, default=None, metavar="MAX_NORM",
                     help="add global gradient-norm clipping to the step")
+    ap.add_argument("--clip-recompute", action="store_true",
+                    help="with --clip: the norm pass writes no G and the update sums the "
+                         "peers again (fewer bytes when R < 4, or R < 2 with an accumulator)")
     ap.add_argument("--groups", action="store_true",
                     help="two parameter groups (no weight decay on 1-D tensors): the grouped "
                          "fused step")
@@ -1005,7 +1019,9 @@ def main():
     log(f"bench: workload {args.workload}, allocating and generating inputs on cuda:0")
     if args.groups and args.clip:
         raise SystemExit("bench.py: --groups and --clip are separate measurements")
-    W = Workload(args.workload, seed, args.clip, args.groups)
+    if args.clip_recompute and not args.clip:
+        raise SystemExit("bench.py: --clip-recompute goes with --clip")
+    W = Workload(args.workload, seed, args.clip, args.groups, args.clip_recompute)
     log(f"bench: n={W.n} R={W.w.R} sets={W.nsets}; warmup {args.warmup}")
     t = 0
     for _ in range(args.warmup):

@@ -597,6 +597,46 @@ def test_clipped_step_two_shards(max_norm):
         assert H.assert_state_close(got, want, f"clipped shard {s}") == 0
 
 
+@pytest.mark.parametrize("R", [2, 8])
+@pytest.mark.parametrize("with_acc", [False, True])
+def test_clipped_step_recompute_equals_stored_g(R, with_acc):
+    """The two ways of clipping give the same bits: the norm pass writing G
+    and the update reading it (R = 0), or the norm pass writing nothing and
+    the update summing the peers (and accumulator) again.  Both against the
+    oracle's clipped step."""
+    import torch
+    n, hp, max_norm = 256 * 8 * 5 + 3, HP, 1e-2
+    scale = sbp.mean_scale(R, 2 if with_acc else 1)
+    peers_h = H.host_peers(91, 1, 0, R, n, 1e-2)
+    peers = [H.from_np_u16(x) for x in peers_h]
+    acc_h = (np.asarray(OS.reduce_peers(H.host_peers(91, 1, 1, R, n, 1e-2)), np.float32)
+             if with_acc else None)
+    acc = H.from_np_f32(acc_h) if with_acc else None
+    G = torch.empty(n, dtype=torch.float32, device=H.dev())
+    sq_a = sbp.grad_sq_norm(peers, acc, scale, n, g_sum_out=G).item()
+    sq_b = sbp.grad_sq_norm(peers, acc, scale, n).item()
+    assert sq_a == sq_b
+    cs, coef = sbp.clip_scale(sq_a, max_norm, scale)
+    assert coef < 1.0
+    th, m, v = _state(92, n)
+    a = [H.from_np_f32(x) for x in (th, m, v)] + [H.empty_u16(n)]
+    b = [H.from_np_f32(x) for x in (th, m, v)] + [H.empty_u16(n)]
+    sbp.adamw_shard([], G, cs, *a, hp, 1)
+    sbp.adamw_shard(peers, acc, cs, *b, hp, 1)
+    torch.cuda.synchronize()
+    for x, y, what in zip(a, b, ("master", "m", "v", "param")):
+        assert torch.equal(x, y), f"recompute and stored G differ in {what}"
+    S = OS.reduce_peers(peers_h)
+    Gh = S if acc_h is None else OS.accumulate(acc_h, S)
+    want_total = OS.grad_sq_norm(Gh, np.float32(scale))
+    assert abs(sq_a - want_total) <= 1e-13 * want_total
+    want_cs = OS.clipped_scale(scale, OS.clip_coef(want_total, max_norm))
+    assert cs == float(want_cs)
+    want = OS.shard_step(peers_h, acc_h, want_cs, th, m, v, hp, 1)
+    got = (H.to_np_f32(b[0]), H.to_np_f32(b[1]), H.to_np_f32(b[2]), H.to_np_u16(b[3]))
+    assert H.assert_state_close(got, want, f"recomputed clipped step R={R}") == 0
+
+
 # ---- layout moves: pack / unpack / shard_of / gather on both plan kinds ---------
 
 # N = 64 is the most ranks gather and unpack_shards take as fans; at N = 80
