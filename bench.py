@@ -408,7 +408,7 @@ def summarize_pmc_kernels(base, command):
     known = CALIBRATION_CALLS * COPY_BYTES
     fs, ws = known / (cf * 1024), known / (cw * 1024)
     lines = ["# HBM traffic of every library kernel against its algorithmic bytes", "",
-             "Commands (rocprofv3, one counter per run; R is the repository root on the GPU box):",
+             "Commands (rocprofv3, one counter per run; R is the repository root where they ran):",
              "", "```", command, "```", "",
              f"Calibration (4 GiB copies, {CALIBRATION_CALLS} calls): bytes read = 1024 x "
              f"FETCH_SIZE x {fs:.4f}, bytes written = 1024 x WRITE_SIZE x {ws:.4f}.  "
