@@ -415,7 +415,11 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
  *   Results are deterministic run to run.  If g_sum_out is given, G (fp32,
  *   unscaled) is also written there, so the update can follow as
  *   sbp_adamw_shard(R = 0, acc = g_sum_out, scale = clipped scale) without
- *   reading the peers again.
+ *   reading the peers again.  Without g_sum_out the update is
+ *   sbp_adamw_shard(the same peers and acc, scale = clipped scale), which
+ *   recomputes G; both give the same bits.  Per element, writing G moves
+ *   2R + 34 bytes in the two calls (+4 with acc) and recomputing 4R + 26
+ *   (+8 with acc): recomputing moves less below R = 4 (R = 2 with acc).
  *   peers, R, acc, scale, n   as in sbp_adamw_shard (R may be 0 with acc)
  *   g_sum_out                 device fp32[n], 16-B aligned, or null
  *   workspace                 device double[workspace_len], 8-B aligned,
