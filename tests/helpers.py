@@ -97,6 +97,45 @@ def assert_state_close(got, want, what, f32_ulps=4, bf16_ulps=1):
     return max(worst, mx)
 
 
+# ---- the squared norm's summation bound ---------------------------------------
+
+def sq_norm_depth(n, gpl):
+    """Longest chain of float64 additions any term of sbp_grad_sq_norm passes
+    through, from the documented fixed shape: a lane adds its 8*gpl squares
+    in order (plus one tail element in the first block), the wave adds by a
+    6-level shuffle tree, the block adds its 4 wave sums in order; each level
+    of the tree over the tile partials adds 8 per lane in order, then the
+    same wave and block steps; levels run while more than 2048 partials are
+    left, and a last one sums what remains."""
+    tiles = max(1, ((n >> 3) + 255) // 256)
+    count = (tiles + gpl - 1) // gpl
+    levels = 1
+    while count > 2048:
+        count = (count + 2047) // 2048
+        levels += 1
+    return 8 * gpl + 1 + 6 + 4 + levels * (8 + 6 + 4)
+
+
+def sq_norm_bound(G, scale, n, gpl):
+    """Bound on |library - oracle| for the squared norm of g = fl(G*scale):
+    the squares are exact in float64 and all terms are >= 0, so a sum whose
+    terms each pass through at most d roundings is within gamma_d * sum
+    (gamma_d = d*u / (1 - d*u), u = 2^-53) of the exact sum; the oracle's
+    correctly rounded sum is within u * sum of it."""
+    g = (np.asarray(G, np.float32) * np.float32(scale)).astype(np.float64)
+    total = float(np.sum(g * g))
+    u = 2.0 ** -53
+    d = sq_norm_depth(n, gpl)
+    return (d * u / (1 - d * u) + u) * total * (1 + 1e-9)  # np.sum's own slack
+
+
+def norm_gpl(R, with_acc):
+    """Groups of 8 per lane the norm pass takes (16 or 32 bytes of loads per
+    group take 4 or 2), as the header's launch description states."""
+    lane_bytes = 16 * R + (32 if with_acc else 0)
+    return 4 if lane_bytes == 16 else 2 if lane_bytes == 32 else 1
+
+
 # ---- seeded inputs on both sides --------------------------------------------
 
 def host_peers(seed, t, k, R, n, sigma, i0=0):

@@ -549,7 +549,8 @@ def test_grad_sq_norm(R, n, write):
         G = acc_h
     want = OS.grad_sq_norm(G, np.float32(scale))
     got = float(sq.item())
-    assert abs(got - want) <= 1e-13 * want, (got, want)
+    bound = H.sq_norm_bound(G, scale, n, H.norm_gpl(R, acc_h is not None))
+    assert abs(got - want) <= bound, (got, want, bound)
     assert got == float(sq2.item())  # deterministic run to run
     if write:
         H.assert_bits_equal(H.to_np_f32(gsum), G, "g_sum_out")
@@ -582,7 +583,9 @@ def test_clipped_step_two_shards(max_norm):
     cs, coef = sbp.clip_scale(total, max_norm, scale)
     Gh = [OS.reduce_peers(H.host_peers(22 + s, 1, 0, R, n, 1e-2)) for s in range(2)]
     want_total = sum(OS.grad_sq_norm(x, np.float32(scale)) for x in Gh)
-    assert abs(total - want_total) <= 1e-13 * want_total
+    # each shard's fixed tree, plus the one host addition of the two totals
+    bound = sum(H.sq_norm_bound(x, scale, n, H.norm_gpl(R, False)) for x in Gh)
+    assert abs(total - want_total) <= bound + 2.0 ** -53 * want_total
     want_cs = OS.clipped_scale(scale, OS.clip_coef(want_total, max_norm))
     assert cs == float(want_cs)
     assert (coef < 1.0) == (max_norm < 1.0)
@@ -629,7 +632,7 @@ def test_clipped_step_recompute_equals_stored_g(R, with_acc):
     S = OS.reduce_peers(peers_h)
     Gh = S if acc_h is None else OS.accumulate(acc_h, S)
     want_total = OS.grad_sq_norm(Gh, np.float32(scale))
-    assert abs(sq_a - want_total) <= 1e-13 * want_total
+    assert abs(sq_a - want_total) <= H.sq_norm_bound(Gh, scale, n, H.norm_gpl(R, with_acc))
     want_cs = OS.clipped_scale(scale, OS.clip_coef(want_total, max_norm))
     assert cs == float(want_cs)
     want = OS.shard_step(peers_h, acc_h, want_cs, th, m, v, hp, 1)
