@@ -444,6 +444,35 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R,
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale,
                           float* clipped_scale, double* coef);
 
+/* ------------------------------------------------------------------------
+ * The squared norm for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc.
+ *
+ * sbp_grad_sq_norm_noalloc: the same computation, result bits and argument
+ *   rules as sbp_grad_sq_norm, with the workspace taken from a static
+ *   device array inside the library instead of from the caller.  Each GPU
+ *   the library runs on holds one such array of
+ *   SBP_NOALLOC_SCRATCH_DOUBLES doubles (8 MiB) until the process ends; its
+ *   address is looked up once per device, on that device's first call.  The
+ *   call allocates and frees nothing.
+ *   n is limited to SBP_NOALLOC_MAX_NUMEL (the largest n whose tile
+ *   partials and tree levels fit the array); a larger n is SBP_ERANGE.
+ *   Every workspace slot is written before it is read within one call, so
+ *   nothing needs clearing between calls.  All calls on one GPU share its
+ *   array: calls that overlap in time on one GPU (two streams, or two
+ *   threads) race and must be ordered by the caller.
+ *   Errors: as sbp_grad_sq_norm (less the workspace checks), SBP_ERANGE
+ *   also for n > SBP_NOALLOC_MAX_NUMEL, SBP_EHIP if the array's device
+ *   address cannot be looked up.
+ * ---------------------------------------------------------------------- */
+#define SBP_NOALLOC_SCRATCH_DOUBLES 1048576 /* 2^20 doubles per GPU       */
+#define SBP_NOALLOC_MAX_NUMEL 2146435079LL   /* 2048 * 1048064 + 7         */
+sbp_status sbp_grad_sq_norm_noalloc(const void* const* peers, int32_t R,
+                                    const float* acc, float scale, int64_t n,
+                                    float* g_sum_out, double* sq_out,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,8 @@ Functions (same names as the C calls without the "sbp_" prefix):
                (+ TensorSet: a plan's per-tensor buffers marshalled once)
   scales       mean_scale, tokens_scale, clip_scale
   shard step   reduce_shard, accumulate_grads, adamw_shard, grad_sq_norm
-               (+ grad_sq_norm_workspace)
+               (+ grad_sq_norm_workspace), grad_sq_norm_noalloc (no workspace
+               argument: the library's static per-GPU scratch)
   groups       group_runs (+ group_table: the run table on a device),
                adamw_shard_grouped
 """
@@ -40,9 +41,12 @@ EXPORTS = (
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
     "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards", "sbp_bucket_plan_per_tensor",
     "sbp_group_runs", "sbp_adamw_shard_grouped", "sbp_unpack_shards",
+    "sbp_grad_sq_norm_noalloc",
 )
 
 MAX_GROUPS = 8
+NOALLOC_SCRATCH_DOUBLES = 1 << 20  # SBP_NOALLOC_SCRATCH_DOUBLES
+NOALLOC_MAX_NUMEL = 2146435079  # SBP_NOALLOC_MAX_NUMEL
 
 
 class SbpError(RuntimeError):
@@ -118,6 +122,9 @@ def lib():
         "sbp_grad_sq_norm": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                               ctypes.c_void_p, ctypes.c_void_p], st),
+        "sbp_grad_sq_norm_noalloc": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p], st),
         "sbp_clip_scale": ([ctypes.c_double, ctypes.c_float, ctypes.c_float,
                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)], st),
         "sbp_bucket_plan_per_tensor": ([_i64p, _i64p, ctypes.c_int32, ctypes.c_int32,
@@ -561,6 +568,30 @@ def grad_sq_norm(peers, acc, scale, n, g_sum_out=None, workspace=None, sq_out=No
         None if acc is None else _f32(acc, "grad_sq_norm acc"), float(scale), int(n),
         None if g_sum_out is None else _f32(g_sum_out, "grad_sq_norm g_sum_out"),
         workspace.data_ptr(), workspace.numel(), sq_out.data_ptr(), _stream(stream, ref)))
+    return sq_out
+
+
+def grad_sq_norm_noalloc(peers, acc, scale, n, sq_out, g_sum_out=None, stream=None):
+    """sbp_grad_sq_norm_noalloc: grad_sq_norm with the library's static
+    per-GPU scratch as the workspace (n <= NOALLOC_MAX_NUMEL).  The caller
+    passes every output, sq_out included: nothing is allocated here either.
+    Calls that overlap on one GPU share the scratch and race."""
+    import torch
+    ref = peers[0] if peers else acc
+    if ref is None:
+        raise ValueError("grad_sq_norm_noalloc: needs peers or an accumulator")
+    if any(p.numel() != n for p in peers) or (acc is not None and acc.numel() != n):
+        raise ValueError("grad_sq_norm_noalloc: peers/acc differ in size")
+    if g_sum_out is not None and g_sum_out.numel() != n:
+        raise ValueError("grad_sq_norm_noalloc: g_sum_out has the wrong size")
+    if sq_out.dtype != torch.float64 or not sq_out.is_cuda or not sq_out.is_contiguous():
+        raise ValueError("grad_sq_norm_noalloc: sq_out must be a contiguous float64 device "
+                         "tensor")
+    _check(lib().sbp_grad_sq_norm_noalloc(
+        _ptrs(peers, "grad_sq_norm_noalloc peers"), len(peers),
+        None if acc is None else _f32(acc, "grad_sq_norm_noalloc acc"), float(scale), int(n),
+        None if g_sum_out is None else _f32(g_sum_out, "grad_sq_norm_noalloc g_sum_out"),
+        sq_out.data_ptr(), _stream(stream, ref)))
     return sq_out
 
 

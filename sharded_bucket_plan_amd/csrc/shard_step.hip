@@ -1053,52 +1053,63 @@ static sbp_status sum_partials(const char* who, double* ws, int64_t count, doubl
 
 int64_t sbp_grad_sq_norm_workspace(int64_t n) { return n < 0 ? -1 : sq_norm_workspace(n); }
 
-sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* acc, float scale,
-                            int64_t n, float* g_sum_out, double* workspace,
-                            int64_t workspace_len, double* sq_out, hipStream_t stream) {
-  const char* who = "sbp_grad_sq_norm";
-  if (R < 0 || R > SBP_MAX_PEERS)
-    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: R must be in 0..16");
-  if (n < 0) return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: n < 0");
-  if (sq_out == nullptr || workspace == nullptr)
-    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: null workspace or result pointer");
+}  // extern "C"
+
+// Validation and launches shared by sbp_grad_sq_norm and its allocation-free
+// variant.  `workspace` may be null only when `scratch_ws` supplies it: then
+// the arguments are checked first and the workspace is fetched afterwards, so
+// a bad argument is reported without touching a device.
+static sbp_status grad_sq_norm_on(const char* who, const void* const* peers, int32_t R,
+                                  const float* acc, float scale, int64_t n, float* g_sum_out,
+                                  double* workspace, int64_t workspace_len, double* sq_out,
+                                  hipStream_t stream, sbp_status (*scratch_ws)(double**, int64_t)) {
+  const std::string w(who);
+  if (R < 0 || R > SBP_MAX_PEERS) return sbp::fail(SBP_EINVAL, w + ": R must be in 0..16");
+  if (n < 0) return sbp::fail(SBP_EINVAL, w + ": n < 0");
+  if (sq_out == nullptr || (workspace == nullptr && scratch_ws == nullptr))
+    return sbp::fail(SBP_EINVAL, w + ": null workspace or result pointer");
   if (!sbp::aligned(sq_out, 8) || !sbp::aligned(workspace, 8))
-    return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: workspace and result must be 8-byte aligned");
-  if (n > SBP_MAX_SHARD_NUMEL)
-    return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm: n above SBP_MAX_SHARD_NUMEL");
+    return sbp::fail(SBP_EALIGN, w + ": workspace and result must be 8-byte aligned");
+  if (n > SBP_MAX_SHARD_NUMEL) return sbp::fail(SBP_ERANGE, w + ": n above SBP_MAX_SHARD_NUMEL");
   const int64_t need = sq_norm_workspace(n);
-  if (workspace_len < need)
-    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: workspace too small (see "
-                                 "sbp_grad_sq_norm_workspace)");
-  if (sbp::overlaps(sq_out, 8, workspace, 8 * need))
-    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: result overlaps the workspace");
-  (void)hipGetLastError();
-  if (n == 0)  // the squared norm of nothing is 0
-    return sum_partials(who, workspace, 0, sq_out, stream);
+  if (scratch_ws == nullptr && workspace_len < need)
+    return sbp::fail(SBP_EINVAL, w + ": workspace too small (see sbp_grad_sq_norm_workspace)");
   Peers P;
-  sbp_status st = collect_peers(who, peers, R, P);
-  if (st != SBP_OK) return st;
-  if (R == 0 && acc == nullptr)
-    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: R == 0 needs an accumulator");
-  if ((acc && !sbp::aligned(acc, 16)) || (g_sum_out && !sbp::aligned(g_sum_out, 16)))
-    return sbp::fail(SBP_EALIGN, "sbp_grad_sq_norm: device arrays must be 16-byte aligned");
-  // outputs (g_sum_out, workspace, sq_out) must not overlap any other buffer
+  if (n > 0) {
+    sbp_status st = collect_peers(who, peers, R, P);
+    if (st != SBP_OK) return st;
+    if (R == 0 && acc == nullptr) return sbp::fail(SBP_EINVAL, w + ": R == 0 needs an accumulator");
+    if ((acc && !sbp::aligned(acc, 16)) || (g_sum_out && !sbp::aligned(g_sum_out, 16)))
+      return sbp::fail(SBP_EALIGN, w + ": device arrays must be 16-byte aligned");
+  }
+  // outputs (g_sum_out, sq_out, and the workspace) must not overlap any other
+  // buffer; the workspace is checked once known
   const void* ptr[4 + SBP_MAX_PEERS];
   int64_t len[4 + SBP_MAX_PEERS];
   int k = 0;
-  ptr[k] = g_sum_out; len[k++] = g_sum_out ? 4 * n : 0;
-  ptr[k] = workspace; len[k++] = 8 * need;
+  ptr[k] = g_sum_out; len[k++] = (g_sum_out && n > 0) ? 4 * n : 0;
   ptr[k] = sq_out; len[k++] = 8;
-  ptr[k] = acc; len[k++] = acc ? 4 * n : 0;
-  for (int32_t r = 0; r < R; ++r) { ptr[k] = peers[r]; len[k++] = 2 * n; }
-  for (int a = 0; a < 3; ++a)
+  ptr[k] = acc; len[k++] = (acc && n > 0) ? 4 * n : 0;
+  for (int32_t r = 0; n > 0 && r < R; ++r) { ptr[k] = peers[r]; len[k++] = 2 * n; }
+  for (int a = 0; a < 2; ++a)
     for (int b = a + 1; b < k; ++b)
       if (sbp::overlaps(ptr[a], len[a], ptr[b], len[b]))
-        return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm: buffers overlap");
+        return sbp::fail(SBP_EINVAL, w + ": buffers overlap");
+  if (scratch_ws != nullptr) {
+    sbp_status st = scratch_ws(&workspace, need);
+    if (st != SBP_OK) return st;
+  }
+  for (int b = 0; b < k; ++b)
+    if (sbp::overlaps(workspace, 8 * need, ptr[b], len[b]))
+      return sbp::fail(SBP_EINVAL, w + (b == 1 ? ": result overlaps the workspace"
+                                               : ": buffers overlap"));
+  (void)hipGetLastError();
+  if (n == 0)  // the squared norm of nothing is 0
+    return sum_partials(who, workspace, 0, sq_out, stream);
   const int lane_bytes = 16 * R + (acc ? 32 : 0);  // per group of 8
   const int gpl = norm_groups_per_lane(lane_bytes);
   constexpr int kNormInflight = SBP_NORM_INFLIGHT_KB;
-  st = dispatch_r(R, [&](auto rc) -> sbp_status {
+  sbp_status st = dispatch_r(R, [&](auto rc) -> sbp_status {
     constexpr int RR = decltype(rc)::value;
     const bool wr = g_sum_out != nullptr;
     auto go = [&](auto kernel, int g) {
@@ -1118,6 +1129,60 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* ac
   });
   if (st != SBP_OK) return st;
   return sum_partials(who, workspace, (tiles_for(n) + gpl - 1) / gpl, sq_out, stream);
+}
+
+// ---- the squared norm without a caller workspace ------------------------------
+// The tile partials and tree levels live in one file-scope device array per
+// GPU.  Its host-side name is not a device address: the address is looked up
+// once per device (with that device current) and only that pointer is passed
+// to kernels.  Every slot the tree reads was written earlier in the same call
+// (one partial per tile, then each level from the one below), so the array is
+// never cleared; calls that overlap on one GPU share it and race.
+static __device__ __align__(256) double scratch[SBP_NOALLOC_SCRATCH_DOUBLES];
+
+static sbp_status scratch_workspace(double** ws, int64_t need) {
+  if (need > SBP_NOALLOC_SCRATCH_DOUBLES)
+    return sbp::fail(SBP_ERANGE, "sbp_grad_sq_norm_noalloc: n needs " + std::to_string(need) +
+                                     " workspace doubles, above the " +
+                                     std::to_string(SBP_NOALLOC_SCRATCH_DOUBLES) +
+                                     " of the static scratch (SBP_NOALLOC_MAX_NUMEL)");
+  static std::mutex mu;
+  static double* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return sbp::fail(SBP_EHIP, std::string("sbp_grad_sq_norm_noalloc: hipGetDevice failed: ") +
+                                   hipGetErrorString(e));
+  if (dev < 0 || dev >= 64)
+    return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm_noalloc: device id outside 0..63");
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return sbp::fail(SBP_EHIP,
+                       std::string("sbp_grad_sq_norm_noalloc: looking up the scratch array "
+                                   "failed: ") + hipGetErrorString(e));
+    addr[dev] = static_cast<double*>(p);
+  }
+  *ws = addr[dev];
+  return SBP_OK;
+}
+
+extern "C" {
+
+sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R, const float* acc, float scale,
+                            int64_t n, float* g_sum_out, double* workspace,
+                            int64_t workspace_len, double* sq_out, hipStream_t stream) {
+  return grad_sq_norm_on("sbp_grad_sq_norm", peers, R, acc, scale, n, g_sum_out, workspace,
+                         workspace_len, sq_out, stream, nullptr);
+}
+
+sbp_status sbp_grad_sq_norm_noalloc(const void* const* peers, int32_t R, const float* acc,
+                                    float scale, int64_t n, float* g_sum_out, double* sq_out,
+                                    hipStream_t stream) {
+  return grad_sq_norm_on("sbp_grad_sq_norm_noalloc", peers, R, acc, scale, n, g_sum_out,
+                         nullptr, 0, sq_out, stream, scratch_workspace);
 }
 
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale, float* clipped_scale,

@@ -32,6 +32,8 @@ def test_header_and_binding_agree():
     assert int(defs["SBP_MAX_GROUPS"]) == sbp.MAX_GROUPS
     for name in ("SBP_OK", "SBP_EINVAL", "SBP_EALIGN", "SBP_ERANGE", "SBP_EHIP", "SBP_ENOMEM"):
         assert int(defs[name]) == getattr(sbp, name), name
+    assert int(defs["SBP_NOALLOC_SCRATCH_DOUBLES"]) == sbp.NOALLOC_SCRATCH_DOUBLES
+    assert int(defs["SBP_NOALLOC_MAX_NUMEL"]) == sbp.NOALLOC_MAX_NUMEL
 
 
 def test_library_exports_every_declared_symbol():
@@ -260,6 +262,33 @@ def test_grad_sq_norm_validates_before_launch():
     big = sbp.MAX_SHARD_NUMEL + 1
     assert f(peers, 2, None, 1.0, big, None, ws, sbp.grad_sq_norm_workspace(big), sq,
              None) == sbp.SBP_ERANGE
+
+
+def test_grad_sq_norm_noalloc_limit_and_validation():
+    """The static scratch holds exactly the workspace of NOALLOC_MAX_NUMEL
+    elements; bad arguments and a larger n are refused on the host, before the
+    scratch's device address is looked up (no call here reaches a device)."""
+    cap, top = sbp.NOALLOC_SCRATCH_DOUBLES, sbp.NOALLOC_MAX_NUMEL
+    assert sbp.grad_sq_norm_workspace(top) == cap
+    assert sbp.grad_sq_norm_workspace(top + 1) == cap + 1
+    assert top >= 1003782656  # the Llama-3-8B 1/8 shard fits
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    f = L.sbp_grad_sq_norm_noalloc
+    peers = (V * 2)(0x100000, 0x200000)
+    sq = V(0x900000)
+    n = 10000
+    assert f(peers, 2, None, 1.0, n, None, None, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, None, V(0x900004), None) == sbp.SBP_EALIGN
+    assert f(peers, 0, None, 1.0, n, None, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 17, None, 1.0, n, None, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, -1, None, sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, n, V(0x300008), sq, None) == sbp.SBP_EALIGN
+    assert f(peers, 2, None, 1.0, n, V(0x100000), sq, None) == sbp.SBP_EINVAL
+    assert f(peers, 2, None, 1.0, top + 1, None, V(1 << 40), None) == sbp.SBP_ERANGE
+    assert "SBP_NOALLOC_MAX_NUMEL" in sbp.lib().sbp_last_error().decode()
+    big = sbp.MAX_SHARD_NUMEL + 1
+    assert f(peers, 2, None, 1.0, big, None, sq, None) == sbp.SBP_ERANGE
 
 
 def _same_split_plan(numels, cap, N, align=8, order="reverse"):
