@@ -79,7 +79,7 @@ def fused_bytes_per_elem(R, acc):
 class Workload:
     """Device buffers and the per-step launches of one workload."""
 
-    def __init__(self, name, seed, clip=None, groups=False, recompute=False):
+    def __init__(self, name, seed, clip=None, groups=False, recompute=False, placement="spread"):
         import torch
         import sharded_bucket_plan_amd as sbp
         import synth
@@ -110,6 +110,10 @@ class Workload:
         mall = 256 << 20
         set_bytes = self.bytes_fused
         self.nsets = 1 if set_bytes >= 4 * mall else max(2, -(-4 * mall // set_bytes))
+        # the step's arrays in spread arenas (one per buffer set) unless the
+        # sets are many small cache-resident ones, where placement is moot
+        self.placement = placement if self.nsets <= 4 else "torch"
+        self.arenas = []
         self.sets = [self._alloc_set(i) for i in range(self.nsets)]
         self.i = 0
         torch.cuda.synchronize()
@@ -120,37 +124,61 @@ class Workload:
     def _f32(self, n):
         return self.torch.empty(n, dtype=self.torch.float32, device=self.dev)
 
+    def _arrays(self):
+        """(name, dtype, numel) of the step's arrays in one buffer set."""
+        w, n, torch = self.w, self.n, self.torch
+        a = [("master", torch.float32, n), ("m", torch.float32, n), ("v", torch.float32, n),
+             ("p", torch.int16, n)]
+        if w.pack:
+            a += [("flat0", torch.int16, n)] + [(f"peer{r}", torch.int16, n)
+                                                 for r in range(1, w.R)]
+        else:
+            a += [(f"mb{k}_{r}", torch.int16, n) for k in range(w.K) for r in range(w.R)]
+        if self.acc:
+            a.append(("acc", torch.float32, n))
+        if self.clip:
+            a.append(("gsum", torch.float32, n))
+        return a
+
     def _alloc_set(self, i):
         w, n, synth = self.w, self.n, self.synth
+        spec = self._arrays()
+        if self.placement == "spread":
+            ar = self.sbp.Arena([k * self.torch.empty(0, dtype=dt).element_size()
+                                 for _, dt, k in spec], seed=0x5EED + i)
+            self.arenas.append(ar)
+            buf = {nm: ar.tensor(j, dt, k) for j, (nm, dt, k) in enumerate(spec)}
+        else:
+            buf = {nm: self.torch.empty(k, dtype=dt, device=self.dev) for nm, dt, k in spec}
         s = {}
-        s["master"] = synth.dev_normal_f32(self._f32(n), self.seed + i, synth.master_stream(0),
+        s["master"] = synth.dev_normal_f32(buf["master"], self.seed + i, synth.master_stream(0),
                                            w.master_sigma)
-        s["m"] = self._f32(n).zero_()
-        s["v"] = self._f32(n).zero_()
-        s["p"] = self._u16(n)
+        s["m"] = buf["m"].zero_()
+        s["v"] = buf["v"].zero_()
+        s["p"] = buf["p"]
         if w.pack:
-            # rank 0 packs its per-tensor gradients; rank 1's contribution is
-            # already in bucket layout (N = 1: bucket layout = shard layout)
+            # rank 0 packs its per-tensor gradients (the backward's outputs,
+            # ordinary allocations); rank 1's contribution is already in
+            # bucket layout (N = 1: bucket layout = shard layout)
             s["grads"] = [synth.dev_normal_bf16(self._u16(k), self.seed + i,
                                                 synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
                           for t, k in enumerate(w.numels)]
-            s["flat0"] = self._u16(n)
+            s["flat0"] = buf["flat0"]
             s["peers"] = [s["flat0"]] + [
-                synth.dev_normal_bf16(self._u16(n), self.seed + i, synth.peer_stream(1, 0, r),
+                synth.dev_normal_bf16(buf[f"peer{r}"], self.seed + i, synth.peer_stream(1, 0, r),
                                       w.grad_sigma) for r in range(1, w.R)]
         else:
-            nmb = w.K
-            s["mb"] = [[synth.dev_normal_bf16(self._u16(n), self.seed + i,
+            s["mb"] = [[synth.dev_normal_bf16(buf[f"mb{k}_{r}"], self.seed + i,
                                               synth.peer_stream(1, k, r), w.grad_sigma)
-                        for r in range(w.R)] for k in range(nmb)]
+                        for r in range(w.R)] for k in range(w.K)]
             s["peers"] = s["mb"][-1]
         if self.acc:
-            s["acc"] = self._f32(n)
+            s["acc"] = buf["acc"]
         # the plain step's buffers marshalled once (the step the timed loop makes)
         s["step"] = self.sbp.ShardStep(s["peers"], s.get("acc"), s["master"], s["m"], s["v"],
                                        s["p"])
         if self.clip:
-            s["gsum"] = self._f32(n)
+            s["gsum"] = buf["gsum"]
             s["ws"] = self.torch.empty(self.sbp.grad_sq_norm_workspace(n),
                                        dtype=self.torch.float64, device=self.dev)
             s["sq"] = self.torch.empty(1, dtype=self.torch.float64, device=self.dev)
@@ -231,7 +259,17 @@ class Workload:
                 "clip_recompute": self.recompute,
                 "param_groups": len(self.groups) if self.groups else 1,
                 "group_runs": int(self.runs[0].numel()) if self.groups else 1,
-                "fused_bytes_per_elem": self.bytes_fused // self.n}
+                "fused_bytes_per_elem": self.bytes_fused // self.n,
+                "placement": self.placement}
+
+    def release(self):
+        """Drops the buffer sets (and frees the arenas once nothing uses them)."""
+        self.sets = []
+        self.arenas = []
+        import gc
+        gc.collect()
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
 
 def _summary_fields(path):
@@ -524,10 +562,11 @@ def cpu_baseline(workload_name, seed, target_s):
                        f"{spent:.1f} s")}
 
 
-def _oracle_core_worker(workload_name, seed, k, target_s, chunk, barrier, results):
-    """One core's share of cpu_oracle_cores: slice k of the shard generated
-    first, then, from the common start, the oracle's fused step on it over
-    and over for `target_s` seconds (its time does not depend on the values)."""
+def _oracle_core_worker(workload_name, seed, k, target_s, chunk, ready, go, results):
+    """One core's share of OracleCores: slice k of the shard generated first,
+    then, once every worker is ready and the parent says go, the oracle's
+    fused step on it over and over for `target_s` seconds (its time does not
+    depend on the values)."""
     import numpy as np
     import synth
     from oracle import step as OS
@@ -540,7 +579,8 @@ def _oracle_core_worker(workload_name, seed, k, target_s, chunk, barrier, result
     z = np.zeros(chunk, np.float32)
     acc = OS.reduce_peers(peers) if w.K > 1 else None
     scale = OS.mean_scale(w.R, w.K)
-    barrier.wait()
+    ready.wait()
+    go.wait()
     t0 = time.perf_counter()
     done = 0
     while time.perf_counter() - t0 < target_s:
@@ -549,41 +589,158 @@ def _oracle_core_worker(workload_name, seed, k, target_s, chunk, barrier, result
     results.put((k, done, time.perf_counter() - t0))
 
 
-def cpu_oracle_cores(workload_name, seed, procs, target_s):
-    """The same oracle on `procs` host cores at once: one worker process per
-    core, each on its own slice of the shard (the step is elementwise, so the
-    slices are independent).  Inputs are generated before a common start;
-    after it each worker runs only the oracle, for about `target_s` seconds.
-    Throughput is all elements done over the longest worker's time.  The
-    worker processes are started from a process that never touches the GPU."""
-    import multiprocessing as mp
-    import synth
+def host_cores():
+    """Host cores this process may use: the affinity mask, capped by
+    OMP_NUM_THREADS where that is set (a GPU machine's share of its host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
-    w = synth.WORKLOADS[workload_name]
-    chunk = 1 << 22
-    ctx = mp.get_context("spawn")
-    barrier = ctx.Barrier(procs)
-    results = ctx.Queue()
-    workers = [ctx.Process(target=_oracle_core_worker,
-                           args=(workload_name, seed, k, target_s, chunk, barrier, results))
-               for k in range(procs)]
-    for p in workers:
-        p.start()
-    res = [results.get(timeout=600) for _ in range(procs)]
-    for p in workers:
-        p.join()
-    if any(p.exitcode != 0 for p in workers):
-        raise RuntimeError("cpu_oracle_cores: a worker failed")
-    done = sum(d for _, d, _ in res)
-    wall = max(t for _, _, t in res)
-    b = fused_bytes_per_elem(w.R, w.K > 1)
-    return {"value": done / wall, "unit": "params/s", "cores": procs, "kind": "oracle",
-            "gbs": done * b / wall / 1e9, "wall_s": wall,
-            "per_core_params_per_s": [d / t for _, d, t in sorted(res)],
-            "host_cpu": host_cpu_model(), "host_threads_available": os.cpu_count(),
-            "sample": (f"{procs} slices of {chunk} elements of the {workload_name} shard, one "
-                       f"per worker process, each stepped repeatedly for {target_s:.0f} s "
-                       f"(one fused step, R={w.R}), numpy binary32 oracle")}
+
+class OracleCores:
+    """The oracle on `procs` host cores at once: one worker process per core,
+    each on its own slice of the shard (the step is elementwise, so the slices
+    are independent).  The workers are spawned (not forked) at construction,
+    which the bench does before it touches the GPU; they generate their
+    inputs and wait.  run() starts them together, each runs only the oracle
+    for about `target_s` seconds, and throughput is all elements done over
+    the longest worker's time."""
+
+    def __init__(self, workload_name, seed, procs, target_s, chunk=1 << 22):
+        import multiprocessing as mp
+        self.workload_name, self.procs, self.target_s, self.chunk = (workload_name, procs,
+                                                                     target_s, chunk)
+        ctx = mp.get_context("spawn")
+        self.ready, self.go = ctx.Barrier(procs + 1), ctx.Barrier(procs + 1)
+        self.results = ctx.Queue()
+        self.workers = [ctx.Process(target=_oracle_core_worker, daemon=True,
+                                    args=(workload_name, seed, k, target_s, chunk, self.ready,
+                                          self.go, self.results))
+                        for k in range(procs)]
+        for p in self.workers:
+            p.start()
+
+    def wait_ready(self):
+        self.ready.wait(timeout=600)
+
+    def run(self):
+        import synth
+        self.go.wait(timeout=600)
+        res = [self.results.get(timeout=600) for _ in range(self.procs)]
+        for p in self.workers:
+            p.join(timeout=60)
+        if any(p.exitcode != 0 for p in self.workers):
+            raise RuntimeError("OracleCores: a worker failed")
+        w = synth.WORKLOADS[self.workload_name]
+        done = sum(d for _, d, _ in res)
+        wall = max(t for _, _, t in res)
+        b = fused_bytes_per_elem(w.R, w.K > 1)
+        return {"value": done / wall, "unit": "params/s", "cores": self.procs, "kind": "oracle",
+                "gbs": done * b / wall / 1e9, "wall_s": wall,
+                "per_core_params_per_s": [d / t for _, d, t in sorted(res)],
+                "host_cpu": host_cpu_model(), "host_threads_available": os.cpu_count(),
+                "sample": (f"{self.procs} slices of {self.chunk} elements of the "
+                           f"{self.workload_name} shard, one per worker process, each stepped "
+                           f"repeatedly for {self.target_s:.0f} s (one fused step, R={w.R}), "
+                           "numpy binary32 oracle")}
+
+
+def cpu_oracle_cores(workload_name, seed, procs, target_s):
+    """OracleCores on its own (no GPU work in this process)."""
+    pool = OracleCores(workload_name, seed, procs, target_s)
+    pool.wait_ready()
+    return pool.run()
+
+
+def _probe_lib():
+    import ctypes
+    from sharded_bucket_plan_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built: run __graft_entry__.build()")
+    L = ctypes.CDLL(PROBE_LIB)
+    L.sbp_probe_stream_mix.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_uint32, ctypes.c_void_p]
+    return L
+
+
+PROBE_VARIANTS = ("8 consecutive per lane", "stores by stream through LDS", "split 4+4")
+
+
+def mix_ceiling(W, t, rounds=3, reps=3):
+    """The ceiling of the fused step's access mix on W's arrays: three
+    zero-arithmetic passes of the same traffic (the measurement kernels of
+    libsbp_probe.so, mask 0: the state is written back unchanged) timed
+    round-robin with the fused step itself, `reps` launches each per round.
+    Returns the best probe rate and the fused step's rate in the same rounds;
+    None where the step is not a plain fused step with R in {1, 2, 8}."""
+    import ctypes
+    import torch
+    w = W.w
+    if W.acc or W.clip or W.groups or w.R not in (1, 2, 8):
+        return None
+    L = _probe_lib()
+    s = W.sets[0]
+    tiles = W.n // 2048
+    peers = (ctypes.c_void_p * w.R)(*[x.data_ptr() for x in s["peers"]])
+    stream = torch.cuda.current_stream().cuda_stream
+    scale = W.scale(t)
+    probe_bytes = fused_bytes_per_elem(w.R, False) * tiles * 2048
+    ms = {k: [] for k in range(len(PROBE_VARIANTS))}
+    fused_ms = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for _ in range(rounds):
+        for k in range(-1, len(PROBE_VARIANTS)):
+            def launch():
+                if k < 0:
+                    s["step"](scale, W.hp, t)
+                else:
+                    rc = L.sbp_probe_stream_mix(k, peers, w.R, s["master"].data_ptr(),
+                                                s["m"].data_ptr(), s["v"].data_ptr(),
+                                                s["p"].data_ptr(), tiles, 0, stream)
+                    if rc != 0:
+                        raise RuntimeError("sbp_probe_stream_mix failed")
+            launch()
+            for a, b in ev:
+                a.record()
+                launch()
+                b.record()
+            torch.cuda.synchronize()
+            (fused_ms if k < 0 else ms[k]).extend(a.elapsed_time(b) for a, b in ev)
+    rates = {PROBE_VARIANTS[k]: probe_bytes / (statistics.median(v) * 1e-3) / 1e9
+             for k, v in ms.items()}
+    best = max(rates.values())
+    fused = W.bytes_fused / (statistics.median(fused_ms) * 1e-3) / 1e9
+    return {"mix_ceiling_gbs": best, "probe_gbs": rates, "fused_gbs_same_rounds": fused,
+            "frac_of_mix_ceiling": fused / best, "rounds": rounds, "launches_per_round": reps}
+
+
+def fused_rate_on(args, seed, placement, warmup, steps):
+    """The workload's fused kernel on buffers of the given placement, in this
+    process: `warmup` steps, then the average of `steps` launches."""
+    import torch
+    W = Workload(args.workload, seed, args.clip, args.groups, args.clip_recompute, placement)
+    t = 0
+    for _ in range(warmup):
+        t += 1
+        W.step(t)
+    torch.cuda.synchronize()
+    evs = [{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for p, _ in W.parts()} for _ in range(steps)]
+    for k in range(steps):
+        t += 1
+        W.step(t, evs[k])
+    torch.cuda.synchronize()
+    ms = [e["fused_adamw_kernel"][0].elapsed_time(e["fused_adamw_kernel"][1]) for e in evs]
+    avg = sum(ms) / len(ms)
+    gbs = W.bytes_fused / (avg * 1e-3) / 1e9
+    out = {"placement": W.placement, "kernel_ms_avg": avg, "gbs": gbs, "frac": gbs / PEAK_GBS}
+    W.release()
+    return out
 
 
 def bucket_sweep(seed, reps=5):
@@ -948,6 +1105,18 @@ def main():
     ap.add_argument("--groups", action="store_true",
                     help="two parameter groups (no weight decay on 1-D tensors): the grouped "
                          "fused step")
+    ap.add_argument("--placement", choices=["spread", "torch"], default="spread",
+                    help="where the step's arrays live: a spread arena (the library's "
+                         "sbp_arena, pages spread over the whole HBM; the default) or "
+                         "ordinary torch allocations")
+    ap.add_argument("--no-compare-placement", action="store_true",
+                    help="skip timing the fused kernel on torch allocations after the "
+                         "spread-arena run")
+    ap.add_argument("--no-mix-ceiling", action="store_true",
+                    help="skip the zero-arithmetic probes of the fused step's access mix")
+    ap.add_argument("--oracle-cores", type=int, default=None, metavar="P",
+                    help="host cores for the all-core oracle baseline (default: this "
+                         "process's share, capped by OMP_NUM_THREADS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--bucket-sweep", action="store_true",
@@ -992,10 +1161,19 @@ def main():
               "shard step is per rank and nothing here crosses GPUs", file=sys.stderr)
         sys.exit(2)
 
-    import torch
+    # the all-core oracle's workers are spawned before anything touches the
+    # GPU; they generate their inputs now and run after the GPU timing
     import synth
-
     seed = synth.SEED if args.seed is None else args.seed
+    modes = (args.bucket_sweep or args.layout or args.layout_call or args.stream_mix
+             or args.calibrate_copy)
+    pool = None
+    cores = args.oracle_cores or host_cores()
+    if not modes and not args.no_cpu_baseline and cores > 1:
+        pool = OracleCores(args.workload, seed, cores, args.cpu_seconds)
+
+    import torch
+
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -1021,13 +1199,17 @@ def main():
         raise SystemExit("bench.py: --groups and --clip are separate measurements")
     if args.clip_recompute and not args.clip:
         raise SystemExit("bench.py: --clip-recompute goes with --clip")
-    W = Workload(args.workload, seed, args.clip, args.groups, args.clip_recompute)
-    log(f"bench: n={W.n} R={W.w.R} sets={W.nsets}; warmup {args.warmup}")
+    W = Workload(args.workload, seed, args.clip, args.groups, args.clip_recompute,
+                 args.placement)
+    log(f"bench: n={W.n} R={W.w.R} sets={W.nsets} placement={W.placement}; "
+        f"warmup {args.warmup}")
     t = 0
     for _ in range(args.warmup):
         t += 1
         W.step(t)
     torch.cuda.synchronize()
+    if pool:
+        pool.wait_ready()  # the oracle workers have their inputs and are idle
     parts = W.parts()
     evs = [{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for p, _ in parts} for _ in range(args.steps)]
@@ -1061,16 +1243,36 @@ def main():
 
     # the committed counters are of the plain fused kernel
     traffic = None if args.groups else traffic_from_profile(bytes_fused)
+    ceiling = None
+    if not args.no_mix_ceiling:
+        ceiling = mix_ceiling(W, t + 1)
+        if ceiling:
+            log(f"bench: access-mix ceiling {ceiling['mix_ceiling_gbs']:.0f} GB/s "
+                f"(zero-arithmetic probes); fused step {ceiling['fused_gbs_same_rounds']:.0f} "
+                f"GB/s in the same rounds = {ceiling['frac_of_mix_ceiling']:.3f} of it")
+    placement = W.placement
+    W.release()
+    del W
+    other = None
+    if placement == "spread" and not args.no_compare_placement:
+        other = fused_rate_on(args, seed, "torch", args.warmup, args.steps)
+        log(f"bench: the same kernel on torch allocations: {other['kernel_ms_avg']:.4f} ms, "
+            f"{other['frac']:.3f} of 8 TB/s")
     copy_gbs = None
     if not args.no_copy_ceiling:
-        del W
         torch.cuda.empty_cache()
         copy_gbs = copy_ceiling_gbs()
         log(f"bench: 4 GiB device copy on this GPU: {copy_gbs:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"bench: CPU baseline (~{args.cpu_seconds:.0f} s of oracle work)")
-        cpu = cpu_baseline(args.workload, seed, args.cpu_seconds)
+        log(f"bench: CPU baseline (~{args.cpu_seconds:.0f} s of oracle work on 1 core"
+            + (f", then on {cores} cores)" if pool else ")"))
+        one = cpu_baseline(args.workload, seed, args.cpu_seconds)
+        if pool:
+            cpu = pool.run()
+            cpu["one_core"] = one
+        else:
+            cpu = one
 
     line = {
         "metric": METRIC,
@@ -1091,7 +1293,13 @@ def main():
                      "kernel": "fused_adamw_kernel", "kernel_ms_avg": kern_avg,
                      "algorithmic_bytes_per_launch": bytes_fused,
                      "copy_gbs_this_gpu": copy_gbs,
-                     "frac_of_copy": (achieved / copy_gbs) if copy_gbs else None},
+                     "frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
+                     "placement": placement,
+                     "mix_ceiling_gbs": ceiling["mix_ceiling_gbs"] if ceiling else None,
+                     "frac_of_mix_ceiling": (achieved / ceiling["mix_ceiling_gbs"]
+                                             if ceiling else None),
+                     "mix_ceiling": ceiling,
+                     "torch_placement": other},
         "cpu_baseline": cpu,
         "kernels": kernels,
     }

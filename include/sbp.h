@@ -34,8 +34,9 @@
  *   - n == 0 (after the count and hyperparameter checks) returns SBP_OK
  *     without reading any pointer or launching anything.
  *   - Device pointers are caller-owned device (HBM) memory.  No call
- *     allocates or frees device memory.  Host arrays are read during the
- *     call only.
+ *     allocates or frees device memory, except the spread arena's
+ *     (sbp_arena_create / sbp_arena_free), whose purpose that is.  Host
+ *     arrays are read during the call only.
  *   - Device calls validate on the host, enqueue on `stream` and return;
  *     a fault in a kernel surfaces at the caller's next synchronisation.
  *   - Before it launches, a device call reads and clears the calling
@@ -443,6 +444,56 @@ sbp_status sbp_grad_sq_norm(const void* const* peers, int32_t R,
                             hipStream_t stream);
 sbp_status sbp_clip_scale(double total_sq, float max_norm, float scale,
                           float* clipped_scale, double* coef);
+
+/* ------------------------------------------------------------------------
+ * Spread arena: device memory for a rank's shard state and receive buffers
+ * ("Parallelisms", ZeRO-1 and ZeRO-3: each rank keeps its shard's fp32
+ * master copy, first and second moments and parameter shard, and receives
+ * its peers' gradient chunks of that shard).  Unlike every call above, these
+ * calls allocate and free device memory; they exist for placement.
+ *
+ * The fused step streams all its arrays at the same offset at once, and on
+ * MI355X that mix runs measurably faster when the arrays' physical pages are
+ * spread over the whole HBM instead of packed into one region.
+ * sbp_arena_create gives each array its own virtual range and backs it with
+ * physical chunks of chunk_bytes taken evenly spaced from a run of chunks
+ * created over spread_bytes of device memory (the chunks in between are
+ * released before the call returns), mapped to the arrays' chunk slots in a
+ * seeded random order.  The policy is fixed (no timing, no search); only the
+ * device's allocator decides where the run lies.
+ *
+ * bytes[n_arrays]  size of each array in bytes (>= 0; 0 gives a null pointer)
+ * n_arrays         1..SBP_ARENA_MAX_ARRAYS
+ * chunk_bytes      physical chunk size: 0 for the default 64 MiB, else a
+ *                  positive multiple of 2 MiB (and of the device's
+ *                  allocation granularity); each array is rounded up to a
+ *                  whole number of chunks, at most 16384 in all
+ * spread_bytes     memory to spread over: 0 for all free device memory less
+ *                  a reserve of 1/32 of the total (at least 1 GiB); at most
+ *                  8192 chunks are created to spread, never fewer than the
+ *                  arrays need
+ * seed             seed of the slot order (splitmix64 + Fisher-Yates)
+ * ptrs[n_arrays]   receive the arrays' device addresses (chunk_bytes-aligned;
+ *                  contents undefined until written)
+ * out              receives the arena; free with sbp_arena_free
+ * The arrays belong to the device current at the call and are readable and
+ * writable from it.  sbp_arena_free synchronises that device, then unmaps
+ * and releases everything; a null arena is a no-op.  sbp_arena_info reports
+ * the chunk size, the chunks kept and the chunks created to spread over
+ * (any output pointer may be null).
+ * Errors: SBP_EINVAL (null, bad count, negative size, bad chunk size),
+ * SBP_ERANGE (more than 16384 chunks), SBP_ENOMEM (device memory), SBP_EHIP
+ * (no virtual memory management, or another runtime failure).  On error
+ * nothing stays allocated.
+ * ---------------------------------------------------------------------- */
+#define SBP_ARENA_MAX_ARRAYS 64
+typedef struct sbp_arena sbp_arena;
+sbp_status sbp_arena_create(const int64_t* bytes, int32_t n_arrays,
+                            int64_t chunk_bytes, int64_t spread_bytes,
+                            uint64_t seed, void** ptrs, sbp_arena** out);
+sbp_status sbp_arena_info(const sbp_arena* arena, int64_t* chunk_bytes,
+                          int64_t* chunks_kept, int64_t* chunks_spread);
+sbp_status sbp_arena_free(sbp_arena* arena);
 
 /* ------------------------------------------------------------------------
  * The squared norm for callers that cannot allocate device memory: code

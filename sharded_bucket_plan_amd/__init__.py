@@ -17,6 +17,8 @@ Functions (same names as the C calls without the "sbp_" prefix):
                argument: the library's static per-GPU scratch)
   groups       group_runs (+ group_table: the run table on a device),
                adamw_shard_grouped
+  placement    Arena (sbp_arena_create / _info / _free): device arrays whose
+               physical pages are spread over the whole device memory
 """
 
 import ctypes
@@ -41,12 +43,13 @@ EXPORTS = (
     "sbp_grad_sq_norm_workspace", "sbp_grad_sq_norm", "sbp_clip_scale",
     "sbp_unpack_params", "sbp_shard_of", "sbp_gather_shards", "sbp_bucket_plan_per_tensor",
     "sbp_group_runs", "sbp_adamw_shard_grouped", "sbp_unpack_shards",
-    "sbp_grad_sq_norm_noalloc",
+    "sbp_grad_sq_norm_noalloc", "sbp_arena_create", "sbp_arena_info", "sbp_arena_free",
 )
 
 MAX_GROUPS = 8
 NOALLOC_SCRATCH_DOUBLES = 1 << 20  # SBP_NOALLOC_SCRATCH_DOUBLES
 NOALLOC_MAX_NUMEL = 2146435079  # SBP_NOALLOC_MAX_NUMEL
+ARENA_MAX_ARRAYS = 64  # SBP_ARENA_MAX_ARRAYS
 
 
 class SbpError(RuntimeError):
@@ -125,6 +128,10 @@ def lib():
         "sbp_grad_sq_norm_noalloc": ([_vpp, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p], st),
+        "sbp_arena_create": ([_i64p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                              ctypes.c_uint64, _vpp, ctypes.POINTER(ctypes.c_void_p)], st),
+        "sbp_arena_info": ([ctypes.c_void_p, _i64p, _i64p, _i64p], st),
+        "sbp_arena_free": ([ctypes.c_void_p], st),
         "sbp_clip_scale": ([ctypes.c_double, ctypes.c_float, ctypes.c_float,
                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)], st),
         "sbp_bucket_plan_per_tensor": ([_i64p, _i64p, ctypes.c_int32, ctypes.c_int32,
@@ -652,3 +659,67 @@ def unpack_shards(plan, shards, params, bucket=-1, stream=None):
     arr = _tensor_array(plan, params, bucket, "unpack_shards params")
     _check(lib().sbp_unpack_shards(plan.handle, int(bucket), _ptrs(shards, "unpack_shards shards"),
                                    arr, _stream(stream, shards[0])))
+
+
+# ---- spread arena ---------------------------------------------------------------
+
+_TYPESTR = {"float32": "<f4", "float64": "<f8", "int16": "<i2", "int32": "<i4", "int64": "<i8",
+            "uint8": "|u1", "bfloat16": "<i2"}
+
+
+class _DeviceView:
+    """A __cuda_array_interface__ view of arena memory; it holds the arena,
+    and torch holds it for as long as a tensor made from it lives."""
+
+    def __init__(self, arena, ptr, numel, typestr):
+        self._arena = arena
+        self.__cuda_array_interface__ = {"shape": (int(numel),), "typestr": typestr,
+                                         "data": (int(ptr), False), "version": 3,
+                                         "strides": None}
+
+
+class Arena:
+    """sbp_arena_create: device arrays of the given byte sizes whose physical
+    chunks are spread evenly over the device memory (chunk 0 = 64 MiB,
+    spread 0 = all free memory less a reserve).  tensor(i, dtype, numel)
+    returns a torch tensor aliasing array i; the arena stays allocated while
+    any such tensor (or this object) is alive, and is freed after the last
+    (sbp_arena_free synchronises the device first)."""
+
+    def __init__(self, nbytes, chunk=0, spread=0, seed=0x5EED):
+        nbytes = [int(b) for b in nbytes]
+        k = len(nbytes)
+        arr = (ctypes.c_int64 * max(k, 1))(*nbytes)
+        ptrs = (ctypes.c_void_p * max(k, 1))()
+        h = ctypes.c_void_p()
+        _check(lib().sbp_arena_create(arr, k, int(chunk), int(spread), int(seed) & (2**64 - 1),
+                                      ptrs, ctypes.byref(h)))
+        self._h = h
+        self.nbytes = nbytes
+        self.ptrs = [ptrs[i] or 0 for i in range(k)]
+
+    def info(self):
+        c, kept, spread = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().sbp_arena_info(self._h, ctypes.byref(c), ctypes.byref(kept),
+                                    ctypes.byref(spread)))
+        return {"chunk_bytes": c.value, "chunks_kept": kept.value, "chunks_spread": spread.value}
+
+    def tensor(self, i, dtype, numel=None):
+        import torch
+        name = str(dtype).replace("torch.", "")
+        item = torch.empty(0, dtype=dtype).element_size()
+        if numel is None:
+            numel = self.nbytes[i] // item
+        if numel * item > self.nbytes[i]:
+            raise ValueError(f"Arena.tensor: {numel} x {item} bytes exceed array {i}")
+        if name not in _TYPESTR:
+            raise ValueError(f"Arena.tensor: unsupported dtype {dtype}")
+        t = torch.as_tensor(_DeviceView(self, self.ptrs[i], numel, _TYPESTR[name]),
+                            device=torch.device("cuda", torch.cuda.current_device()))
+        return t.view(dtype) if name == "bfloat16" else t
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.sbp_arena_free(h)
+            self._h = None

@@ -8,6 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsbp.so")
+# measurement kernels for bench.py only (not part of the library's ABI)
+PROBE_LIB = os.path.join(PKG, "libsbp_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -28,15 +30,20 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + sources()
+def _hipcc(srcs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
         print(r.stderr)
+
+
+def build(verbose=False):
+    _hipcc(sources(), LIB, verbose)
+    _hipcc(sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), PROBE_LIB, verbose)
     return LIB
 
 

@@ -34,6 +34,7 @@ def test_header_and_binding_agree():
         assert int(defs[name]) == getattr(sbp, name), name
     assert int(defs["SBP_NOALLOC_SCRATCH_DOUBLES"]) == sbp.NOALLOC_SCRATCH_DOUBLES
     assert int(defs["SBP_NOALLOC_MAX_NUMEL"]) == sbp.NOALLOC_MAX_NUMEL
+    assert int(defs["SBP_ARENA_MAX_ARRAYS"]) == sbp.ARENA_MAX_ARRAYS
 
 
 def test_library_exports_every_declared_symbol():
@@ -289,6 +290,32 @@ def test_grad_sq_norm_noalloc_limit_and_validation():
     assert "SBP_NOALLOC_MAX_NUMEL" in sbp.lib().sbp_last_error().decode()
     big = sbp.MAX_SHARD_NUMEL + 1
     assert f(peers, 2, None, 1.0, big, None, sq, None) == sbp.SBP_ERANGE
+
+
+def test_arena_validates_before_touching_a_device():
+    """Bad arena arguments come back as error codes before any HIP call (no
+    device here: a valid request then fails at the device lookup)."""
+    L = sbp.lib()
+    V = ctypes.c_void_p
+    I = ctypes.c_int64
+    p, h = (V * 2)(), V()
+    two = (I * 2)(100, 200)
+    assert L.sbp_arena_create(None, 2, 0, 0, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create(two, 2, 0, 0, 1, None, ctypes.byref(h)) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create(two, 2, 0, 0, 1, p, None) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create(two, 0, 0, 0, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create(two, 65, 0, 0, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    for chunk in (-(2 << 20), 3 << 20, 1 << 20, 4096):
+        assert L.sbp_arena_create(two, 2, chunk, 0, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create(two, 2, 0, -1, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    assert L.sbp_arena_create((I * 2)(-1, 5), 2, 0, 0, 1, p, ctypes.byref(h)) == sbp.SBP_EINVAL
+    # 16384 chunks at most: 32 GiB of 2 MiB chunks fit, one byte more does not
+    assert L.sbp_arena_create((I * 1)((32 << 30) + 1), 1, 2 << 20, 0, 1, p,
+                              ctypes.byref(h)) == sbp.SBP_ERANGE
+    assert L.sbp_arena_create((I * 2)(1 << 62, 1 << 62), 2, 0, 0, 1, p,
+                              ctypes.byref(h)) == sbp.SBP_ERANGE
+    assert L.sbp_arena_free(None) == sbp.SBP_OK
+    assert L.sbp_arena_info(None, None, None, None) == sbp.SBP_EINVAL
 
 
 def _same_split_plan(numels, cap, N, align=8, order="reverse"):
