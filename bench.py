@@ -336,6 +336,59 @@ def _pmc_rows(d, counter):
     return rows
 
 
+def _pmc_dispatches(d):
+    """[(kernel name, {counter: value})] of every dispatch in rocprofv3 counter
+    CSVs under d, in dispatch order."""
+    import csv
+    import glob
+    by = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = int(r["Dispatch_Id"])
+                name, ctr = by.setdefault(k, (r.get("Kernel_Name", ""), {}))
+                ctr[r["Counter_Name"]] = ctr.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [by[k] for k in sorted(by)]
+
+
+def summarize_sweep_pmc(pmc_dir, sweep_json, rates_json, command):
+    """Markdown table of the DRAM credit stalls per launch of --placement-sweep
+    --sweep-quick under rocprofv3 --pmc (the sweep's launch log names each
+    dispatch), beside the rates of a plain --placement-sweep run."""
+    sw = json.loads(open(sweep_json).read().strip().splitlines()[-1])
+    rates = json.loads(open(rates_json).read().strip().splitlines()[-1]) if rates_json else None
+    keep = ("fused_adamw_kernel", "mix_probe", "copy_probe")
+    disp = [d for d in _pmc_dispatches(pmc_dir) if any(k in d[0] for k in keep)]
+    log_ = [tuple(x) for x in sw["launches"]]
+    if len(disp) != len(log_):
+        raise SystemExit(f"{len(disp)} dispatches against {len(log_)} logged launches")
+    last = {}
+    for (sname, label), (_, ctr) in zip(log_, disp):
+        if label != "touch":
+            last[(sname, label)] = ctr  # the timed launch follows the warm one
+    counters = sorted({c for ctr in last.values() for c in ctr})
+    labels = list(dict.fromkeys(label for (_, label) in last))
+    sets = sw["phase_a_sets"]
+    lines = ["Command (repository root R on the GPU box, TMPDIR=/tmp, cwd /tmp):", "",
+             "```", command, "```", "",
+             f"Box: {sw.get('box')}" + (f"; rates from a separate `--placement-sweep` run on "
+                                        f"box {rates.get('box')}" if rates else ""), ""]
+    for label in labels:
+        lines += [f"**{label}** (counters per launch, millions)", "",
+                  "| set | " + " | ".join(c.replace("TCC_EA0_", "").replace("_sum", "")
+                                        for c in counters)
+                  + (" | % of 8 TB/s |" if rates else " |"),
+                  "|---|" + "---|" * (len(counters) + (1 if rates else 0))]
+        for sname in sets:
+            ctr = last.get((sname, label), {})
+            row = [f"{ctr.get(c, float('nan')) / 1e6:.2f}" for c in counters]
+            if rates:
+                row.append(f"{rates['phase_a'].get(label, {}).get(sname, float('nan')):.2f}")
+            lines.append(f"| {sname} | " + " | ".join(row) + " |")
+        lines.append("")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, command):
     """Write the committed HBM-traffic summary of the fused kernel from four
     rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, on the benchmark and on
@@ -503,6 +556,22 @@ def summarize_pmc_kernels(base, command):
     return "\n".join(lines) + "\n"
 
 
+def box_identity():
+    """Which machine and GPU a measurement ran on (MI355X boxes differ)."""
+    import socket
+    out = {"host": socket.gethostname()}
+    try:
+        import torch
+        prop = torch.cuda.get_device_properties(0)
+        out["gpu"] = prop.name
+        uuid = getattr(prop, "uuid", None)
+        if uuid is not None:
+            out["gpu_uuid"] = str(uuid)
+    except Exception:  # identity is informative only
+        pass
+    return out
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -662,8 +731,11 @@ def _probe_lib():
     L = ctypes.CDLL(PROBE_LIB)
     L.sbp_probe_stream_mix.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                       ctypes.c_uint32, ctypes.c_void_p]
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_uint32, ctypes.c_int,
+                                       ctypes.c_uint, ctypes.c_void_p]
+    L.sbp_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_uint, ctypes.c_void_p]
     return L
 
 
@@ -687,6 +759,7 @@ def mix_ceiling(W, t, rounds=3, reps=3):
     tiles = W.n // 2048
     peers = (ctypes.c_void_p * w.R)(*[x.data_ptr() for x in s["peers"]])
     stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device=W.dev)
     scale = W.scale(t)
     probe_bytes = fused_bytes_per_elem(w.R, False) * tiles * 2048
     ms = {k: [] for k in range(len(PROBE_VARIANTS))}
@@ -701,7 +774,8 @@ def mix_ceiling(W, t, rounds=3, reps=3):
                 else:
                     rc = L.sbp_probe_stream_mix(k, peers, w.R, s["master"].data_ptr(),
                                                 s["m"].data_ptr(), s["v"].data_ptr(),
-                                                s["p"].data_ptr(), tiles, 0, stream)
+                                                s["p"].data_ptr(), sink.data_ptr(), tiles, 0,
+                                                1, 64, stream)
                     if rc != 0:
                         raise RuntimeError("sbp_probe_stream_mix failed")
             launch()
@@ -717,6 +791,168 @@ def mix_ceiling(W, t, rounds=3, reps=3):
     fused = W.bytes_fused / (statistics.median(fused_ms) * 1e-3) / 1e9
     return {"mix_ceiling_gbs": best, "probe_gbs": rates, "fused_gbs_same_rounds": fused,
             "frac_of_mix_ceiling": fused / best, "rounds": rounds, "launches_per_round": reps}
+
+
+# The probe family of --placement-sweep: (label, kind, variant, blocks per
+# CU, XCD chunk, bytes per element of the Llama shard's traffic mix)
+SWEEP = ([("fused step (library kernel)", "fused", None, None, None, 42)]
+         + [(f"8/lane, stores at end, {b} blk/CU, C64", "probe", 0, b, 64, 42)
+            for b in (1, 2, 3, 4)]
+         + [("8/lane, stores at end, uncapped, C64", "probe", 0, 0, 64, 42)]
+         + [(f"8/lane, stores at end, 1 blk/CU, C{c}", "probe", 0, 1, c, 42)
+            for c in (1, 16, 32, 256)]
+         + [("8/lane, stores at end, 1 blk/CU, one eighth per XCD", "probe", 0, 1, 0, 42)]
+         + [(f"stores by stream through LDS, {b} blk/CU", "probe", 1, b, 64, 42) for b in (1, 2)]
+         + [(f"loads and stores by stream through LDS, {b} blk/CU", "probe", 7, b, 64, 42)
+            for b in (1, 2)]
+         + [(f"split 4+4, {b} blk/CU", "probe", 2, b, 64, 42) for b in (1, 2, 4)]
+         + [(f"16 consecutive/lane, {b} blk/CU", "probe", 5, b, 64, 42) for b in (1, 2)]
+         + [(f"2 x 8, 256 groups apart, {b} blk/CU", "probe", 6, b, 64, 42) for b in (1, 2)]
+         + [(f"read-only (11 streams), {b or 'uncapped'} blk/CU", "probe", 3, b, 64, 28)
+            for b in (1, 2, 0)]
+         + [(f"write-only (4 streams), {b or 'uncapped'} blk/CU", "probe", 4, b, 64, 14)
+            for b in (1, 2, 4, 0)]
+         + [(f"copy 4 GiB, {b or 'uncapped'} blk/CU", "copy", None, b, 64, None)
+            for b in (2, 4, 8, 0)])
+SWEEP_QUICK = (0, 1, 22, 26)  # fused, 8/lane at 1 blk/CU, read-only at 1, write-only at 2
+
+
+def placement_sweep(seed, passes=3, reps=3, quick=False, compact_sets=9, spread_sets=3):
+    """The stream-mix probe family (libsbp_probe.so) and the library's fused
+    R = 8 step on the Llama-3-8B shard's 12 arrays (n rounded down to whole
+    tiles), on many physical placements held at once, timed round-robin:
+      phase A  `compact_sets` arenas made with no spread (each array's chunks
+               created one after another), allocated in sequence, so together
+               they walk through the HBM; the fused step, the 8/lane probe
+               and the read-only and write-only halves of the mix;
+      phase B  (after A's arenas are freed) `spread_sets` spread arenas, then
+               one set of torch allocations; every variant of the family.
+    Rates are % of 8 TB/s from the median of `reps` launches per pass."""
+    import ctypes
+    import torch
+    import sharded_bucket_plan_amd as sbp
+    import synth
+
+    L = _probe_lib()
+    w = synth.WORKLOADS["llama3_8b"]
+    n_shard = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+    tiles = n_shard // 2048
+    n = tiles * 2048
+    R = w.R
+    sizes = [4 * n] * 3 + [2 * n] + [2 * n] * R  # master, m, v, out, peers
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    hp = sbp.AdamW(w.adamw.lr, w.adamw.beta1, w.adamw.beta2, w.adamw.eps, w.adamw.weight_decay)
+    copy_a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    copy_b = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+
+    def arrays_of(ptrs):
+        return {"master": ptrs[0], "m": ptrs[1], "v": ptrs[2], "out": ptrs[3],
+                "peers": (ctypes.c_void_p * R)(*ptrs[4:4 + R])}
+
+    launches = []  # (set, label) of every kernel launch, in order
+
+    def launch(item, a, t, sname=""):
+        label, kind, var, bpc, C, _ = item
+        launches.append((sname, label))
+        if kind == "fused":
+            h = sbp.AdamWHParams.of(hp, t, "sweep")
+            rc = sbp.lib().sbp_adamw_shard(a["peers"], R, None, 0.125, a["master"], a["m"],
+                                           a["v"], a["out"], n, ctypes.byref(h), stream)
+        elif kind == "copy":
+            rc = L.sbp_probe_copy(copy_a.data_ptr(), copy_b.data_ptr(), COPY_BYTES, bpc, C,
+                                  stream)
+        else:
+            rc = L.sbp_probe_stream_mix(var, a["peers"], R, a["master"], a["m"], a["v"],
+                                        a["out"], sink.data_ptr(), tiles, 0, bpc, C, stream)
+        if rc != 0:
+            raise RuntimeError(f"sweep launch failed: {label}")
+
+    def nbytes(item):
+        return 2 * COPY_BYTES if item[1] == "copy" else item[5] * n
+
+    def run(sets, items, tag):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        ms = {}
+        for p in range(passes):
+            for sname, a in sets:
+                for item in items:
+                    if item[1] == "copy" and sname != sets[0][0]:
+                        continue
+                    launch(item, a, 1, sname)
+                    for x, y in ev:
+                        x.record()
+                        launch(item, a, 1, sname)
+                        y.record()
+                    torch.cuda.synchronize()
+                    ms.setdefault((item[0], sname), []).extend(x.elapsed_time(y) for x, y in ev)
+            log(f"sweep {tag}: pass {p + 1}/{passes}")
+        table = {}
+        for item in items:
+            row = {}
+            for sname, _ in sets:
+                v = ms.get((item[0], sname))
+                if v:
+                    row[sname] = round(nbytes(item) / (statistics.median(v) * 1e-3) / 1e9
+                                       / PEAK_GBS * 100, 2)
+            table[item[0]] = row
+        return table
+
+    def touch(a, sname):  # write every page once (the write-only probe, no cap)
+        launches.append((sname, "touch"))
+        if L.sbp_probe_stream_mix(4, a["peers"], R, a["master"], a["m"], a["v"], a["out"],
+                                  sink.data_ptr(), tiles, 0, 0, 64, stream) != 0:
+            raise RuntimeError("sweep: touch failed")
+        for k in range(R):  # peers: a copy over each of them
+            p = a["peers"][k]
+            launches.append((sname, "touch"))
+            if L.sbp_probe_copy(copy_a.data_ptr(), p, (2 * n) // 16384 * 16384, 0, 64,
+                                stream) != 0:
+                raise RuntimeError("sweep: touch failed")
+
+    out = {"n": n, "R": R, "passes": passes, "launches_per_pass": reps,
+           "unit": "% of 8 TB/s (algorithmic bytes / median launch time)",
+           "box": box_identity()}
+    log(f"sweep: box {out['box']}")
+    # phase A: compact arenas, allocated in sequence through the HBM
+    items_a = [SWEEP[i] for i in SWEEP_QUICK]
+    arenas, sets = [], []
+    for k in range(compact_sets):
+        ar = sbp.Arena(sizes, spread=sum(-(-b // (64 << 20)) for b in sizes) * (64 << 20),
+                       seed=k)
+        free, _ = torch.cuda.mem_get_info()
+        log(f"sweep: compact set {k} allocated; {free / 1e9:.1f} GB free")
+        arenas.append(ar)
+        sets.append((f"compact{k}", arrays_of(ar.ptrs)))
+        touch(sets[-1][1], sets[-1][0])
+    torch.cuda.synchronize()
+    out["phase_a"] = run(sets, items_a, "A")
+    out["phase_a_sets"] = [s for s, _ in sets]
+    del arenas, sets
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    if quick:
+        out["launches"] = launches
+        return out
+    # phase B: spread arenas, then torch allocations
+    arenas, sets, keep = [], [], []
+    for k in range(spread_sets):
+        ar = sbp.Arena(sizes, seed=100 + k)
+        arenas.append(ar)
+        sets.append((f"spread{k}", arrays_of(ar.ptrs)))
+        touch(sets[-1][1], sets[-1][0])
+        log(f"sweep: spread set {k} allocated ({ar.info()['chunks_spread']} chunks spread over)")
+    ts = [torch.empty(b, dtype=torch.uint8, device=dev) for b in sizes]
+    keep.append(ts)
+    sets.append(("torch", arrays_of([t.data_ptr() for t in ts])))
+    touch(sets[-1][1], sets[-1][0])
+    torch.cuda.synchronize()
+    out["phase_b"] = run(sets, SWEEP, "B")
+    out["phase_b_sets"] = [s for s, _ in sets]
+    return out
 
 
 def fused_rate_on(args, seed, placement, warmup, steps):
@@ -1117,6 +1353,17 @@ def main():
     ap.add_argument("--oracle-cores", type=int, default=None, metavar="P",
                     help="host cores for the all-core oracle baseline (default: this "
                          "process's share, capped by OMP_NUM_THREADS)")
+    ap.add_argument("--placement-sweep", action="store_true",
+                    help="only run the stream-mix probe family and the fused step over many "
+                         "physical placements of the Llama shard's arrays and print its JSON")
+    ap.add_argument("--sweep-quick", action="store_true",
+                    help="with --placement-sweep: phase A only, one pass, one launch each "
+                         "(for counter runs)")
+    ap.add_argument("--summarize-sweep-pmc", nargs=4,
+                    metavar=("PMC_DIR", "SWEEP_QUICK_JSON", "RATES_JSON", "CMD"),
+                    help="print the DRAM credit-stall table of a counter run of "
+                         "--placement-sweep --sweep-quick (RATES_JSON: a plain sweep's output, "
+                         "or '')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--bucket-sweep", action="store_true",
@@ -1146,6 +1393,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_sweep_pmc:
+        print(summarize_sweep_pmc(*args.summarize_sweep_pmc), end="")
+        return
     if args.summarize_pmc_kernels:
         print(summarize_pmc_kernels(*args.summarize_pmc_kernels), end="")
         return
@@ -1166,7 +1416,7 @@ def main():
     import synth
     seed = synth.SEED if args.seed is None else args.seed
     modes = (args.bucket_sweep or args.layout or args.layout_call or args.stream_mix
-             or args.calibrate_copy)
+             or args.calibrate_copy or args.placement_sweep)
     pool = None
     cores = args.oracle_cores or host_cores()
     if not modes and not args.no_cpu_baseline and cores > 1:
@@ -1189,6 +1439,13 @@ def main():
         return
     if args.stream_mix:
         print(json.dumps(stream_mix(seed)), flush=True)
+        return
+    if args.placement_sweep:
+        if args.sweep_quick:
+            res = placement_sweep(seed, passes=1, reps=1, quick=True, compact_sets=9)
+        else:
+            res = placement_sweep(seed)
+        print(json.dumps(res), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps({"copy_gbs": copy_ceiling_gbs(CALIBRATION_CALLS - 1),
@@ -1302,6 +1559,7 @@ def main():
                      "torch_placement": other},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "box": box_identity(),
     }
     print(json.dumps(line), flush=True)
 
