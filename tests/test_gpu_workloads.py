@@ -1,8 +1,10 @@
-"""GPU parity on the five synthetic workloads, in the launch configuration the
-benchmark times.  Where the oracle finishes in seconds the comparison is over
-every element; at full model scale it is over sampled elements, which the
-oracle computes one by one (the step is elementwise once the plan is fixed,
-and the inputs of any element can be regenerated on their own)."""
+"""GPU parity on the five synthetic workloads, in the launch configuration and
+placement the benchmark times.  The comparison is over every element, at
+model scale too: there the oracle runs slice by slice in worker processes on
+the host's cores (tests/oracle_pool.py; the step is elementwise once the plan
+is fixed, and the inputs of any element can be regenerated on their own).
+The all-gather side at full scale is compared over sampled elements, which the
+oracle computes one by one."""
 
 import numpy as np
 import pytest
@@ -160,195 +162,205 @@ def _sampled_state(dth, dm, dv, dp, idx):
             H.to_np_f32(_gather(dv, idx_d)), H.to_np_u16(_gather(dp, idx_d)))
 
 
-def test_llama3_8b_shard_sampled():
-    """Llama-3-8B ZeRO-3 shard (N=8, R=8, 1.0B elements): the benchmark's
-    workload and launch, two steps, sampled elements."""
+def _compare_slices(results, arrays, recompute, what, every=8):
+    """Compares the oracle workers' digests of each slice with digests of the
+    GPU's copy of the same slice; a differing slice is recomputed here and
+    compared element by element (the assertion then names the element)."""
+    from tests import oracle_pool as OPL
+    done = 0
+    for job, want in results:
+        i0, i1 = job[2], job[3]
+        got_arrays = [H.to_np_f32(a[i0:i1]) for a in arrays[:3]] + [H.to_np_u16(arrays[3][i0:i1])]
+        if OPL.digests(got_arrays) != want:
+            exp = recompute(job)
+            for x, y, name in zip(got_arrays, exp, ("master", "m", "v", "param")):
+                H.assert_bits_equal(x, y, f"{what} {name} in [{i0}, {i1})")
+            raise AssertionError(f"{what}: digests of [{i0}, {i1}) differ but the arrays agree")
+        done += 1
+        if done % every == 0:
+            print(f"{what}: {done} slices equal (through element {i1})", flush=True)
+    return done
+
+
+def _arena_state(n, R, K=1, with_acc=False):
+    """The step's arrays in one spread arena, as bench.py places them:
+    master, m, v, param shard, then K microbatches of R peers (+ acc)."""
+    import torch
+    sizes = [4 * n] * 3 + [2 * n] + [2 * n] * (R * K) + ([4 * n] if with_acc else [])
+    a = sbp.Arena(sizes)
+    th, m, v = (a.tensor(j, torch.float32, n) for j in range(3))
+    p = a.tensor(3, torch.int16, n)
+    mb = [[a.tensor(4 + k * R + r, torch.int16, n) for r in range(R)] for k in range(K)]
+    acc = a.tensor(4 + R * K, torch.float32, n) if with_acc else None
+    return a, th, m, v, p, mb, acc
+
+
+def test_llama3_8b_shard_full():
+    """Llama-3-8B ZeRO-3 shard (N=8, R=8, 1,003,782,656 elements): the
+    benchmark's workload, launch and placement (a spread arena), two steps,
+    every element of master, m, v and the bf16 shard against the oracle run
+    slice by slice on the host's cores."""
+    from tests import oracle_pool as OPL
     import torch
     w = synth.WORKLOADS["llama3_8b"]
     hp = _hp(w)
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n = pl.shard_numel
     assert n == 1003782656
-    f32 = lambda: torch.empty(n, dtype=torch.float32, device=H.dev())
-    dth, dm, dv = f32(), f32(), f32()
-    synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
-    dm.zero_()
-    dv.zero_()
-    dp = H.empty_u16(n)
-    idx = _sample_index(pl, n, 1 << 18, 1)
-    th = synth.normal_f32_at(SEED, synth.master_stream(0), idx, w.master_sigma)
-    want = (th, np.zeros_like(th), np.zeros_like(th), None)
-    bufs = None
-    for t in (1, 2):
-        bufs = H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, bufs)
-        sbp.adamw_shard(bufs, None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
-        peers_h = [synth.normal_bf16_at(SEED, synth.peer_stream(t, 0, r), idx, w.grad_sigma)
-                   for r in range(w.R)]
-        want = OS.shard_step(peers_h, None, OS.mean_scale(w.R), want[0], want[1], want[2], hp, t)
-    torch.cuda.synchronize()
-    got = _sampled_state(dth, dm, dv, dp, idx)
-    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"llama3_8b {name}")
+    jobs = [("llama3_8b", SEED, i0, min(n, i0 + OPL.SLICE), 2) for i0 in range(0, n, OPL.SLICE)]
+    with OPL.pool() as pool:
+        results = pool.imap(OPL.shard_digests, jobs)  # the host works while the GPU does
+        arena, dth, dm, dv, dp, mb, _ = _arena_state(n, w.R)
+        synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+        dm.zero_()
+        dv.zero_()
+        for t in (1, 2):
+            H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, mb[0])
+            sbp.adamw_shard(mb[0], None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
+        torch.cuda.synchronize()
+        print(f"llama3_8b: GPU steps done; comparing {len(jobs)} slices", flush=True)
+        done = _compare_slices(results, (dth, dm, dv, dp),
+                               lambda job: OPL.shard_state(job), "llama3_8b")
+    assert done == len(jobs)
 
 
-def test_llama3_8b_grouped_sampled():
+def test_llama3_8b_grouped_full():
     """The Llama-3-8B shard with the benchmark's two parameter groups (decay on
     matrices, none on the 1-D tensors; bench.py --groups): two grouped steps,
-    sampled elements.  A sampled element's group is that of the tensor owning
-    its flat position under the oracle's plan (rank 0 owns chunk 0 of every
-    bucket; this plan has no padding); the sample adds the first and last
-    shard element of every 1-D tensor piece, so both groups and every group
-    boundary are in it."""
+    every element against the oracle's grouped step run slice by slice on the
+    host's cores (each element's group found through the oracle's plan)."""
+    from tests import oracle_pool as OPL
     import torch
     w = synth.WORKLOADS["llama3_8b"]
     hp = _hp(w)
     tg = [1 if len(shape) == 1 else 0 for _, shape in w.params]
     groups = [(hp.lr, hp.weight_decay), (hp.lr, 0.0)]
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
-    opl = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n = pl.shard_numel
-    rs, rg = sbp.group_table(pl, 0, tg, H.dev())
-    f32 = lambda: torch.empty(n, dtype=torch.float32, device=H.dev())
-    dth, dm, dv = f32(), f32(), f32()
-    synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
-    dm.zero_()
-    dv.zero_()
-    dp = H.empty_u16(n)
-    # shard positions of rank 0 <-> flat positions, from the oracle plan
-    so = np.array([b.shard_offset for b in opl.buckets], np.int64)
-    fo = np.array([b.flat_offset for b in opl.buckets], np.int64)
-    ch = np.array([b.chunk for b in opl.buckets], np.int64)
-    extra = []
-    for t, (_, shape) in enumerate(w.params):
-        if len(shape) != 1:
-            continue
-        a = opl.tensor_flat_offset(t)
-        e = a + w.numels[t]
-        for b in range(len(opl.buckets)):  # rank 0's chunk of bucket b: [fo, fo + ch)
-            lo, hi = max(a, fo[b]), min(e, fo[b] + ch[b])
-            if lo < hi:
-                extra += [so[b] + lo - fo[b], so[b] + hi - 1 - fo[b]]
-    idx = np.unique(np.concatenate([_sample_index(pl, n, 1 << 18, 4),
-                                    np.array(extra, np.int64)]))
-    bk = np.searchsorted(so, idx, side="right") - 1
-    flat = fo[bk] + (idx - so[bk])
-    starts = np.array([opl.tensor_flat_offset(t) for t in range(len(w.numels))], np.int64)
-    order = np.argsort(starts)
-    tids = order[np.searchsorted(starts[order], flat, side="right") - 1]
-    assert np.all(flat - starts[tids] < np.array(w.numels)[tids])  # no padding
-    elem_group = np.array(tg, np.int64)[tids]
-    assert set(np.unique(elem_group)) == {0, 1}
-    th = synth.normal_f32_at(SEED, synth.master_stream(0), idx, w.master_sigma)
-    want = (th, np.zeros_like(th), np.zeros_like(th), None)
-    bufs = None
-    for t in (1, 2):
-        bufs = H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, bufs)
-        sbp.adamw_shard_grouped(bufs, None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t,
-                                groups, rs, rg)
-        peers_h = [synth.normal_bf16_at(SEED, synth.peer_stream(t, 0, r), idx, w.grad_sigma)
-                   for r in range(w.R)]
-        want = OS.shard_step_grouped(peers_h, None, OS.mean_scale(w.R), want[0], want[1],
-                                     want[2], hp, groups, elem_group, t)
-    torch.cuda.synchronize()
-    got = _sampled_state(dth, dm, dv, dp, idx)
-    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"llama3_8b grouped {name}")
+    jobs = [("llama3_8b", SEED, i0, min(n, i0 + OPL.SLICE), 2) for i0 in range(0, n, OPL.SLICE)]
+    # both groups occur (a slice holding a 1-D tensor's piece and a matrix's)
+    g = OPL.shard0_groups("llama3_8b", 0, n)
+    assert set(np.unique(g)) == {0, 1}
+    with OPL.pool() as pool:
+        results = pool.imap(OPL.grouped_digests, jobs)
+        rs, rg = sbp.group_table(pl, 0, tg, H.dev())
+        arena, dth, dm, dv, dp, mb, _ = _arena_state(n, w.R)
+        synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+        dm.zero_()
+        dv.zero_()
+        for t in (1, 2):
+            H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, mb[0])
+            sbp.adamw_shard_grouped(mb[0], None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t,
+                                    groups, rs, rg)
+        torch.cuda.synchronize()
+        print(f"llama3_8b grouped: GPU steps done; comparing {len(jobs)} slices", flush=True)
+        done = _compare_slices(results, (dth, dm, dv, dp),
+                               lambda job: OPL.grouped_state(job), "llama3_8b grouped")
+    assert done == len(jobs)
 
 
-def test_gpt_7b5_accumulate_tokens_sampled():
-    """'7.5B'-labelled GPT shard (N=64, R=8): 4 microbatches, the first three
-    accumulated bucket by bucket, the last fused; 1/C valid-token scaling."""
+def test_gpt_7b5_accumulate_tokens_full():
+    """'7.5B'-labelled GPT shard (N=64, R=8, 103,890,048 elements): 4
+    microbatches, the first three accumulated bucket by bucket, the last
+    fused; 1/C valid-token scaling; two steps; every element against the
+    oracle run slice by slice on the host's cores."""
+    from tests import oracle_pool as OPL
     import torch
     w = synth.WORKLOADS["gpt_7b5"]
     hp = _hp(w)
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n = pl.shard_numel
     assert n == 103890048
-    f32 = lambda: torch.empty(n, dtype=torch.float32, device=H.dev())
-    dth, dm, dv, acc = f32(), f32(), f32(), f32()
-    synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
-    dm.zero_()
-    dv.zero_()
-    dp = H.empty_u16(n)
-    idx = _sample_index(pl, n, 1 << 18, 2)
-    th = synth.normal_f32_at(SEED, synth.master_stream(0), idx, w.master_sigma)
-    want = (th, np.zeros_like(th), np.zeros_like(th), None)
-    bufs = None
-    ranges = [(pl.bucket(b)["shard_offset"], pl.bucket(b)["chunk"]) for b in range(pl.num_buckets)]
-    for t in (1, 2):
-        counts = [synth.tokens(SEED, t, r) for r in range(w.R)]
-        scale = sbp.tokens_scale(counts)
-        A = None
-        for k in range(w.K):
-            bufs = H.dev_peers(SEED, t, k, w.R, n, w.grad_sigma, bufs)
-            peers_h = [synth.normal_bf16_at(SEED, synth.peer_stream(t, k, r), idx, w.grad_sigma)
-                       for r in range(w.R)]
-            if k < w.K - 1:
-                for o, c in ranges:
-                    sbp.accumulate_grads(acc[o:o + c], [b[o:o + c] for b in bufs], first=(k == 0))
-                A = OS.accumulate(A, OS.reduce_peers(peers_h))
-            else:
-                sbp.adamw_shard(bufs, acc, scale, dth, dm, dv, dp, hp, t)
-                want = OS.shard_step(peers_h, A, OS.tokens_scale(counts), want[0], want[1],
-                                     want[2], hp, t)
-    torch.cuda.synchronize()
-    got = _sampled_state(dth, dm, dv, dp, idx)
-    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"gpt_7b5 {name}")
+    step = OPL.SLICE // 4
+    jobs = [("gpt_7b5", SEED, i0, min(n, i0 + step), 2) for i0 in range(0, n, step)]
+    with OPL.pool() as pool:
+        results = pool.imap(OPL.shard_digests, jobs)
+        arena, dth, dm, dv, dp, mb, acc = _arena_state(n, w.R, w.K, with_acc=True)
+        synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+        dm.zero_()
+        dv.zero_()
+        ranges = [(pl.bucket(b)["shard_offset"], pl.bucket(b)["chunk"])
+                  for b in range(pl.num_buckets)]
+        for t in (1, 2):
+            scale = sbp.tokens_scale([synth.tokens(SEED, t, r) for r in range(w.R)])
+            for k in range(w.K):
+                H.dev_peers(SEED, t, k, w.R, n, w.grad_sigma, mb[k])
+                if k < w.K - 1:
+                    for o, c in ranges:
+                        sbp.accumulate_grads(acc[o:o + c], [x[o:o + c] for x in mb[k]],
+                                             first=(k == 0))
+                else:
+                    sbp.adamw_shard(mb[k], acc, scale, dth, dm, dv, dp, hp, t)
+        torch.cuda.synchronize()
+        print(f"gpt_7b5: GPU steps done; comparing {len(jobs)} slices", flush=True)
+        done = _compare_slices(results, (dth, dm, dv, dp),
+                               lambda job: OPL.shard_state(job), "gpt_7b5")
+    assert done == len(jobs)
 
 
-def test_llama3_8b_dp_pack_and_step_sampled():
-    """Llama-3-8B as a full DP replica (N=1, R=2, 8.03B elements): rank 0's 291
-    per-tensor gradients packed into the 162 buckets, rank 1's bucket-layout
-    gradient as the other contribution, one fused step; sampled elements."""
+def test_llama3_8b_dp_pack_and_step_full():
+    """Llama-3-8B as a full DP replica (N=1, R=2, 8.03B elements): rank 0's
+    291 per-tensor gradients packed into the 162 buckets, rank 1's
+    bucket-layout gradient as the other contribution, one fused step.  Every
+    element of every bucket (the packed gradient, master, m, v and the bf16
+    parameters) against the oracle run slice by slice on the host's cores;
+    the first, the last and the largest bucket and 8 seeded random others
+    are compared first."""
+    from tests import oracle_pool as OPL
     import torch
     w = synth.WORKLOADS["llama3_8b_dp"]
     hp = _hp(w)
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
-    opl = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n = pl.shard_numel
     assert n == 8030261248 == pl.flat_numel
+    B = pl.num_buckets
+    info = [pl.bucket(b) for b in range(B)]
+    largest = max(range(B), key=lambda b: info[b]["padded"])
+    rng = np.random.default_rng(11)
+    others = [b for b in range(B) if b not in (0, B - 1, largest)]
+    chosen = sorted({0, B - 1, largest} | set(int(x) for x in rng.choice(others, 8, replace=False)))
+    jobs = []
+    for b in chosen + [b for b in range(B) if b not in chosen]:
+        o, c = info[b]["shard_offset"], info[b]["chunk"]
+        jobs += [("llama3_8b_dp", SEED, i0, min(o + c, i0 + OPL.SLICE))
+                 for i0 in range(o, o + c, OPL.SLICE)]
     t = 1
-    grads = []
-    for tid, k in enumerate(w.numels):
-        g = H.empty_u16(k)
-        synth.dev_normal_bf16(g, SEED, synth.tensor_stream(t, 0, 0, tid), w.grad_sigma)
-        grads.append(g)
-    flat0 = H.empty_u16(n)
-    sbp.pack_grads(pl, grads, flat0)
-    del grads
-    peer1 = H.empty_u16(n)
-    synth.dev_normal_bf16(peer1, SEED, synth.peer_stream(t, 0, 1), w.grad_sigma)
-    f32 = lambda: torch.empty(n, dtype=torch.float32, device=H.dev())
-    dth, dm, dv = f32(), f32(), f32()
-    synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
-    dm.zero_()
-    dv.zero_()
-    dp = H.empty_u16(n)
-    sbp.adamw_shard([flat0, peer1], None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
-    torch.cuda.synchronize()
-    idx = _sample_index(pl, n, 1 << 18, 3)
-    # oracle side: rank 0's packed value at each sampled flat index, element by element
-    starts = np.array([opl.tensor_flat_offset(x) for x in range(len(w.numels))])
-    order = np.argsort(starts)
-    pos = np.searchsorted(starts[order], idx, side="right") - 1
-    tids = order[pos]
-    within = idx - starts[tids]
-    assert np.all(within < np.array(w.numels)[tids])  # this plan has no padding
-    p0 = np.empty(idx.size, np.uint16)
-    for tid in np.unique(tids):
-        sel = tids == tid
-        p0[sel] = synth.normal_bf16_at(SEED, synth.tensor_stream(t, 0, 0, int(tid)), within[sel],
-                                       w.grad_sigma)
-    idx_d = torch.from_numpy(idx).to(H.dev())
-    H.assert_bits_equal(H.to_np_u16(flat0.index_select(0, idx_d)), p0, "packed rank-0 grads")
-    p1 = synth.normal_bf16_at(SEED, synth.peer_stream(t, 0, 1), idx, w.grad_sigma)
-    th = synth.normal_f32_at(SEED, synth.master_stream(0), idx, w.master_sigma)
-    z = np.zeros_like(th)
-    want = OS.shard_step([p0, p1], None, OS.mean_scale(w.R), th, z, z, hp, t)
-    got = _sampled_state(dth, dm, dv, dp, idx)
-    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"llama3_8b_dp {name}")
+    with OPL.pool() as pool:
+        results = pool.imap(OPL.dp_digests, jobs)
+        sizes = [4 * n] * 3 + [2 * n] * 3  # master, m, v, param, rank 0 flat, rank 1
+        arena = sbp.Arena(sizes)
+        dth, dm, dv = (arena.tensor(j, torch.float32, n) for j in range(3))
+        dp, flat0, peer1 = (arena.tensor(j, torch.int16, n) for j in range(3, 6))
+        grads = []
+        for tid, k in enumerate(w.numels):
+            g = H.empty_u16(k)
+            synth.dev_normal_bf16(g, SEED, synth.tensor_stream(t, 0, 0, tid), w.grad_sigma)
+            grads.append(g)
+        sbp.pack_grads(pl, grads, flat0)
+        del grads
+        synth.dev_normal_bf16(peer1, SEED, synth.peer_stream(t, 0, 1), w.grad_sigma)
+        synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+        dm.zero_()
+        dv.zero_()
+        sbp.adamw_shard([flat0, peer1], None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
+        torch.cuda.synchronize()
+        print(f"llama3_8b_dp: GPU step done; comparing all {B} buckets ({chosen} first) in "
+              f"{len(jobs)} slices", flush=True)
+        done = 0
+        for job, want in results:
+            i0, i1 = job[2], job[3]
+            got = ([H.to_np_f32(x[i0:i1]) for x in (dth, dm, dv)]
+                   + [H.to_np_u16(dp[i0:i1]), H.to_np_u16(flat0[i0:i1])])
+            if OPL.digests(got) != want:
+                exp = OPL.dp_state(job)
+                for x, y, name in zip(got, exp, ("master", "m", "v", "param", "packed rank 0")):
+                    H.assert_bits_equal(x, y, f"llama3_8b_dp {name} in [{i0}, {i1})")
+                raise AssertionError(f"llama3_8b_dp: digests of [{i0}, {i1}) differ")
+            done += 1
+            if done % 32 == 0:
+                print(f"llama3_8b_dp: {done} slices equal (through element {i1})", flush=True)
+    assert done == len(jobs)
+    assert sum(j[3] - j[2] for j in jobs) == n
 
 
 @pytest.mark.parametrize("kind", ["whole", "per_tensor"])
