@@ -221,10 +221,10 @@ sbp_status sbp_pack_grads(const sbp_plan* plan, int32_t bucket,
 
 /* ------------------------------------------------------------------------
  * The all-gather side and the local halves of the collectives
- * ("Parallelisms", ZeRO-1: reduce-scatter gives each worker the reduced
- * shard it owns, and an all-gather of the updated shards restores the
- * complete model; FSDP / Flat parameter: the original parameters are views
- * into the flat buffer).  Same copy engine and conventions as pack (16-byte
+ * ("Parallelisms", ZeRO-1: a rank receives its owned shard of the summed
+ * gradient from the reduce-scatter, and all-gathering the updated shards
+ * gives every rank the whole model back; FSDP / Flat parameter: each
+ * original parameter is a view into the flat buffer).  Same copy engine and conventions as pack (16-byte
  * vector path when both sides are 16-B aligned, element-wise otherwise; no
  * device allocation; bucket = -1 for all buckets).
  *
@@ -402,9 +402,9 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Global gradient-norm clipping ("Parallelisms", ZeRO-2: clipping needs the
- * norm over all gradient shards before any weight is updated, and only an
- * all-reduce of the ranks' local squared norms).
+ * Global gradient-norm clipping ("Parallelisms", ZeRO-2: the clip norm is
+ * the all-reduced sum of the ranks' local squared norms, known before the
+ * update).
  *
  * sbp_grad_sq_norm: this rank's squared norm of the normalised gradient,
  *   sum_i (double) g_i^2 with g_i = fl(G_i * scale), G as in sbp_adamw_shard

@@ -79,8 +79,8 @@ def chunk(plan, flat, s):
 def gather(plan, shards):
     """All-gather: put every rank's shard back into the flat bucket layout.
 
-    "Parallelisms", section ZeRO-1: workers all-gather the updated parameter
-    shards, restoring the complete model on every worker.
+    "Parallelisms", section ZeRO-1: after the update each rank's parameter
+    shard is all-gathered, so every rank again holds the whole model.
     """
     if len(shards) != plan.world_n:
         raise ValueError("one shard per rank")
@@ -273,10 +273,10 @@ CLIP_EPS = 1e-6  # added to the norm before dividing (the common convention)
 def grad_sq_norm(G, scale):
     """Sum over this rank's shard of g*g, g = fl(G*scale), in float64.
 
-    "Parallelisms", section ZeRO-2: global gradient-norm clipping needs the
-    norm over all gradient shards before any weight is updated, and only an
-    all-reduce of local squared norms.  Each square of a binary32 value is
-    exact in float64; math.fsum gives the correctly rounded float64 sum.
+    "Parallelisms", section ZeRO-2: the clip norm is the all-reduced sum of
+    the ranks' local squared norms, known before the update.  Each square of
+    a binary32 value is exact in float64; math.fsum gives the correctly
+    rounded float64 sum.
     """
     g = normalise(G, scale).astype(np.float64)
     return math.fsum((g * g).tolist())

@@ -513,12 +513,32 @@ def test_clip_coefficient_and_clipped_norm():
     assert S.clipped_scale(scale, 1.0) == scale
     max_norm = float(np.float32(norm / 4))  # a binary32 hyperparameter
     c = S.clip_coef(sq, max_norm)
-    assert c == max_norm / (norm + 1e-6)
+    assert 0.24 < c < 0.26  # a quarter, less the 1e-6 in the denominator
     cs = S.clipped_scale(scale, c)
     clipped = math.sqrt(S.grad_sq_norm(G, cs))
     assert abs(clipped / max_norm - 1) < 1e-6  # the clipped gradient has the target norm
     assert math.isnan(S.clip_coef(float("nan"), 1.0))  # NaN propagates
     assert S.clip_coef(float("inf"), 1.0) == 0.0
+
+
+def test_clip_coefficient_golden():
+    """Hand-worked coefficients and clipped scales (tests/golden/clip_coef.txt):
+    dyadic norms where the 1e-6 rounds away, a zero norm, the binary32
+    reading of max_norm, and a tiny norm the 1e-6 dominates."""
+    rows = 0
+    for ln in read_golden("clip_coef.txt"):
+        f = ln.split()
+        if f[0] == "coef":
+            got = S.clip_coef(float.fromhex(f[1]), float(f[2]))
+            assert got == float.fromhex(f[3]), ln
+        elif f[0] == "bound":
+            got = S.clip_coef(float.fromhex(f[1]), float(f[2]))
+            assert float(f[3]) < got < float(f[4]), (ln, got)
+        else:
+            got = S.clipped_scale(np.float32(float.fromhex(f[1])), float.fromhex(f[2]))
+            assert float(got) == float.fromhex(f[3]), ln
+        rows += 1
+    assert rows == 10
 
 
 def test_clip_matches_torch_clip_grad_norm():
