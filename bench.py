@@ -323,6 +323,32 @@ def copy_ceiling_gbs(reps=5):
     return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
+def footprint_copy_gbs(nbytes, nsets, reps=20):
+    """A plain streaming copy on the same footprint as a small workload's
+    step: nbytes moved per launch (nbytes/2 read, nbytes/2 written), nsets
+    rotating buffer pairs as the step rotates its sets; HIP events around
+    every launch, average."""
+    import torch
+    half = max(4, nbytes // 2 // 4 * 4)
+    pairs = [(torch.empty(half // 4, dtype=torch.float32, device="cuda:0"),
+              torch.empty(half // 4, dtype=torch.float32, device="cuda:0")) for _ in range(nsets)]
+    for src, dst in pairs:
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k, (a, b) in enumerate(ev):
+        src, dst = pairs[k % nsets]
+        a.record()
+        torch.neg(src, out=dst)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    del pairs
+    torch.cuda.empty_cache()
+    return 2 * half / (ms * 1e-3) / 1e9
+
+
 def _pmc_rows(d, counter):
     """(kernel name, value) of every dispatch in rocprofv3 counter CSVs under d."""
     import csv
@@ -1508,6 +1534,7 @@ def main():
                 f"(zero-arithmetic probes); fused step {ceiling['fused_gbs_same_rounds']:.0f} "
                 f"GB/s in the same rounds = {ceiling['frac_of_mix_ceiling']:.3f} of it")
     placement = W.placement
+    nsets = W.nsets
     W.release()
     del W
     other = None
@@ -1515,11 +1542,15 @@ def main():
         other = fused_rate_on(args, seed, "torch", args.warmup, args.steps)
         log(f"bench: the same kernel on torch allocations: {other['kernel_ms_avg']:.4f} ms, "
             f"{other['frac']:.3f} of 8 TB/s")
-    copy_gbs = None
+    copy_gbs = copy_fp = None
     if not args.no_copy_ceiling:
         torch.cuda.empty_cache()
         copy_gbs = copy_ceiling_gbs()
         log(f"bench: 4 GiB device copy on this GPU: {copy_gbs:.0f} GB/s")
+        if nsets > 1:  # a small workload: also a copy of its own footprint
+            copy_fp = footprint_copy_gbs(bytes_fused, nsets)
+            log(f"bench: copy of the same footprint ({bytes_fused / 1e6:.0f} MB per launch, "
+                f"{nsets} rotating sets): {copy_fp:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: CPU baseline (~{args.cpu_seconds:.0f} s of oracle work on 1 core"
@@ -1551,6 +1582,8 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_fused,
                      "copy_gbs_this_gpu": copy_gbs,
                      "frac_of_copy": (achieved / copy_gbs) if copy_gbs else None,
+                     "copy_gbs_same_footprint": copy_fp,
+                     "frac_of_copy_same_footprint": (achieved / copy_fp) if copy_fp else None,
                      "placement": placement,
                      "mix_ceiling_gbs": ceiling["mix_ceiling_gbs"] if ceiling else None,
                      "frac_of_mix_ceiling": (achieved / ceiling["mix_ceiling_gbs"]
