@@ -1118,7 +1118,8 @@ def layout_call(seed, workload, plan_kind, call, warmup, steps):
     shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
                                     synth.peer_stream(1, 0, r), w.grad_sigma)
               for r in range(w.world_n)]
-    tensors = [torch.empty(k, dtype=torch.int16, device=dev) for k in w.numels]
+    tensors = [torch.empty(k + 8, dtype=torch.int16, device=dev)[misalign:misalign + k]
+               for k in w.numels]
     for t, x in enumerate(tensors):
         synth.dev_normal_bf16(x, seed, synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
     tset = sbp.TensorSet(pl, tensors)
@@ -1149,7 +1150,7 @@ def layout_call(seed, workload, plan_kind, call, warmup, steps):
             "gbs": (rd + wr) / (med * 1e-3) / 1e9}
 
 
-def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
+def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5, misalign=0):
     """The layout calls on a workload's model (default Llama-3-8B at N = 8:
     162 buckets of 291 tensors, 8,030,261,248 elements) under one plan kind
     (whole: tensors whole in capped buckets; split: fixed-size buckets with
@@ -1164,7 +1165,10 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     `reps`, twice: as a Python call (host marshalling included) and as a
     replay of a graph holding the call's launches k times (GPU time, which
     the roofline figures use; k spreads the graph's own launch cost); algorithmic bytes are one read and one write per element
-    moved (a zero-filled padding element is a write only)."""
+    moved (a zero-filled padding element is a write only).  misalign = E > 0
+    makes every per-tensor buffer a view E elements into a larger
+    allocation, so pack reads and unpack writes 2E bytes off 16-byte
+    alignment (as views into a larger parameter buffer are)."""
     import statistics as st
     import torch
     import sharded_bucket_plan_amd as sbp
@@ -1179,7 +1183,8 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
     shards = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
                                     synth.peer_stream(1, 0, r), w.grad_sigma)
               for r in range(w.world_n)]
-    tensors = [torch.empty(k, dtype=torch.int16, device=dev) for k in w.numels]
+    tensors = [torch.empty(k + 8, dtype=torch.int16, device=dev)[misalign:misalign + k]
+               for k in w.numels]
     for t, x in enumerate(tensors):
         synth.dev_normal_bf16(x, seed, synth.tensor_stream(1, 0, 0, t), w.grad_sigma)
     tset = sbp.TensorSet(pl, tensors)  # the same buffers, marshalled once
@@ -1254,7 +1259,7 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5):
         plans[name] = {"us_per_plan": (time.perf_counter() - t0) / 200 * 1e6}
         log(f"layout: {name} {plans[name]['us_per_plan']:.1f} us per plan")
     return {"layout_moves": out, "plans": plans, "workload": workload, "plan": plan_kind,
-            "N": w.world_n,
+            "misalign_elements": misalign, "N": w.world_n,
             "shard_numel": n, "flat_numel": F, "tensors": len(w.numels),
             "buckets": pl.num_buckets}
 
@@ -1400,6 +1405,9 @@ def main():
     ap.add_argument("--plan", choices=["whole", "split", "per_tensor"], default="whole",
                     help="with --layout: the plan whose layout is timed (whole-tensor buckets, "
                          "fixed-size split buckets, or one bucket per tensor with row shards)")
+    ap.add_argument("--misalign", type=int, default=0, metavar="E",
+                    help="with --layout: every per-tensor buffer a view E (0..7) elements into "
+                         "a larger allocation")
     ap.add_argument("--layout-call", choices=sorted(LAYOUT_CALL_BYTES),
                     help="only make this layout call --warmup + --steps times, eagerly, on "
                          "--workload's model under --plan (a counter pass of one kernel)")
@@ -1457,7 +1465,10 @@ def main():
         print(json.dumps(bucket_sweep(seed)), flush=True)
         return
     if args.layout:
-        print(json.dumps(layout_moves(seed, args.workload, args.plan)), flush=True)
+        if not 0 <= args.misalign <= 7:
+            raise SystemExit("bench.py: --misalign takes 0..7 elements")
+        print(json.dumps(layout_moves(seed, args.workload, args.plan, misalign=args.misalign)),
+              flush=True)
         return
     if args.layout_call:
         print(json.dumps(layout_call(seed, args.workload, args.plan, args.layout_call,

@@ -24,7 +24,11 @@
 //     the chunk starts, uniform per block, so it runs on scalar loads of the
 //     kernel arguments;
 //   - a chunk is 256 lanes x 16 bytes, fully coalesced, when source and
-//     destination are 16-byte aligned; otherwise element by element.
+//     destination are 16-byte aligned; otherwise the destination's unaligned
+//     head and tail go element by element and the body in aligned 16-byte
+//     stores, its source read as aligned words and realigned in registers
+//     (a tensor at an odd element offset, as align = 1 and split plans make,
+//     or a view into a larger buffer).
 // gather and unpack_shards read across the N shards, which as segments is one
 // per rank for every bucket or tensor piece (GPT-2 small under the per-tensor
 // plan: 1,184 segments, eight launches).  They go out as fans instead: the N
@@ -96,13 +100,53 @@ __device__ __forceinline__ int find_seg(const SegList& L, int64_t c) {
   return lo;
 }
 
-// `cnt` (at most kChunk) elements from s (null: +0) to d, by one block;
-// `vec`: both 16-byte aligned.
-__device__ __forceinline__ void copy_chunk(uint16_t* d, const uint16_t* s, int64_t cnt, bool vec) {
-  if (vec) {
+// 16 bytes of a byte stream that starts `sh` bytes (even, 2..14) into the
+// aligned word a, continuing into the aligned word b: v_alignbyte takes 4
+// bytes at a byte offset out of two concatenated dwords.  sh is uniform
+// across the block, so the switch does not diverge.
+__device__ __forceinline__ uint4 realign16(uint4 a, uint4 b, uint32_t sh) {
+  const uint32_t r = sh & 3;  // 0 or 2: bytes into the dword
+  uint32_t D[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  switch (sh >> 2) {
+    case 0:
+      return make_uint4(__builtin_amdgcn_alignbyte(D[1], D[0], r),
+                        __builtin_amdgcn_alignbyte(D[2], D[1], r),
+                        __builtin_amdgcn_alignbyte(D[3], D[2], r),
+                        __builtin_amdgcn_alignbyte(D[4], D[3], r));
+    case 1:
+      return make_uint4(__builtin_amdgcn_alignbyte(D[2], D[1], r),
+                        __builtin_amdgcn_alignbyte(D[3], D[2], r),
+                        __builtin_amdgcn_alignbyte(D[4], D[3], r),
+                        __builtin_amdgcn_alignbyte(D[5], D[4], r));
+    case 2:
+      return make_uint4(__builtin_amdgcn_alignbyte(D[3], D[2], r),
+                        __builtin_amdgcn_alignbyte(D[4], D[3], r),
+                        __builtin_amdgcn_alignbyte(D[5], D[4], r),
+                        __builtin_amdgcn_alignbyte(D[6], D[5], r));
+    default:
+      return make_uint4(__builtin_amdgcn_alignbyte(D[4], D[3], r),
+                        __builtin_amdgcn_alignbyte(D[5], D[4], r),
+                        __builtin_amdgcn_alignbyte(D[6], D[5], r),
+                        __builtin_amdgcn_alignbyte(D[7], D[6], r));
+  }
+}
+
+// `cnt` (at most kChunk) elements from s (null: +0) to d, by one block.
+// Both 16-byte aligned: 16-byte loads and stores.  Otherwise the elements
+// before d's first 16-byte boundary and after its last are copied one by
+// one, and the body between goes out in aligned 16-byte stores; its source,
+// `sh` bytes past a 16-byte boundary, is read as whole aligned 16-byte words
+// and realigned in registers.  The last word read ends inside the aligned
+// 16 bytes that hold the body's last source byte, so it never touches a page
+// the source does not.
+__device__ __forceinline__ void copy_chunk(uint16_t* d, const uint16_t* s, int64_t cnt) {
+  const uint32_t dmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(d) & 15);
+  const uint32_t smis = s ? static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s) & 15) : 0;
+  const int t = threadIdx.x;
+  if (dmis == 0 && smis == 0) {
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-      const int64_t e = static_cast<int64_t>(k) * kBlock * 8 + threadIdx.x * 8;
+      const int64_t e = static_cast<int64_t>(k) * kBlock * 8 + t * 8;
       if (e + 8 <= cnt) {
         uint4 x = s ? *reinterpret_cast<const uint4*>(s + e) : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(d + e) = x;
@@ -110,9 +154,87 @@ __device__ __forceinline__ void copy_chunk(uint16_t* d, const uint16_t* s, int64
         for (int64_t j = e; j < cnt; ++j) d[j] = s ? s[j] : 0;
       }
     }
-  } else {
-    for (int64_t j = threadIdx.x; j < cnt; j += kBlock) d[j] = s ? s[j] : 0;
+    return;
   }
+  // every load of the lane (its head element, body words and tail element)
+  // goes out before any store: one memory round trip per block
+  const int64_t head0 = static_cast<int64_t>(((16 - dmis) & 15) >> 1);
+  const int64_t head = head0 < cnt ? head0 : cnt;
+  const int64_t words = (cnt - head) >> 3;  // at most kRounds * kBlock
+  const int64_t tail0 = head + (words << 3);
+  const bool in_head = t < head, in_tail = tail0 + t < cnt;
+  uint16_t hv = 0, tv = 0;
+  uint4 x[kRounds];
+  uint4* db = reinterpret_cast<uint4*>(d + head);
+  if (s == nullptr) {
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) x[k] = make_uint4(0, 0, 0, 0);
+  } else {
+    if (in_head) hv = s[t];
+    if (in_tail) tv = s[tail0 + t];
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(s + head);
+    const uint32_t sh = static_cast<uint32_t>(sb & 15);
+    const uint4* sa = reinterpret_cast<const uint4*>(sb - sh);
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int64_t w = t + static_cast<int64_t>(k) * kBlock;
+      if (w < words) x[k] = sh == 0 ? sa[w] : realign16(sa[w], sa[w + 1], sh);
+    }
+  }
+  if (in_head) d[t] = hv;
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int64_t w = t + static_cast<int64_t>(k) * kBlock;
+    if (w < words) db[w] = x[k];
+  }
+  if (in_tail) d[tail0 + t] = tv;
+}
+
+// Block ci of a segment of `len` elements whose destination is not 16-byte
+// aligned (or whose source is not): the destination's aligned 16-byte words
+// are numbered from its first 16-byte boundary, and block ci writes words
+// [ci * W, (ci + 1) * W), W = kRounds * kBlock, so every word is written
+// whole by one block; the elements before the first boundary (block 0) and
+// after the last whole word (the last block) go one by one.  No word is left
+// half-written by two blocks at every chunk boundary, as cutting at element
+// chunks would.  Sources as in copy_chunk (aligned words, realigned).
+__device__ __forceinline__ void copy_words(uint16_t* d, const uint16_t* s, int64_t len,
+                                           int64_t ci) {
+  constexpr int64_t W = static_cast<int64_t>(kRounds) * kBlock;
+  const int t = threadIdx.x;
+  const uint32_t dmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(d) & 15);
+  const int64_t head0 = static_cast<int64_t>(((16 - dmis) & 15) >> 1);
+  const int64_t head = head0 < len ? head0 : len;
+  const int64_t words = (len - head) >> 3;
+  const int64_t tail0 = head + (words << 3);
+  const int64_t last_ci = (len - 1) / kChunk;
+  const bool in_head = ci == 0 && t < head;
+  const bool in_tail = ci == last_ci && tail0 + t < len;
+  uint16_t hv = 0, tv = 0;
+  uint4 x[kRounds];
+  uint4* db = reinterpret_cast<uint4*>(d + head);
+  if (s == nullptr) {
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) x[k] = make_uint4(0, 0, 0, 0);
+  } else {
+    if (in_head) hv = s[t];
+    if (in_tail) tv = s[tail0 + t];
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(s + head);
+    const uint32_t sh = static_cast<uint32_t>(sb & 15);
+    const uint4* sa = reinterpret_cast<const uint4*>(sb - sh);
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int64_t w = ci * W + t + static_cast<int64_t>(k) * kBlock;
+      if (w < words) x[k] = sh == 0 ? sa[w] : realign16(sa[w], sa[w + 1], sh);
+    }
+  }
+  if (in_head) d[t] = hv;
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int64_t w = ci * W + t + static_cast<int64_t>(k) * kBlock;
+    if (w < words) db[w] = x[k];
+  }
+  if (in_tail) d[tail0 + t] = tv;
 }
 
 __global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
@@ -122,12 +244,17 @@ __global__ void __launch_bounds__(kBlock) copy_kernel(SegList L) {
   if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
   const int64_t c = b;
   const DevSeg sg = L.seg[find_seg(L, c)];
-  const int64_t start = (c - sg.first_chunk) * kChunk;
+  const int64_t ci = c - sg.first_chunk;
+  const bool aligned = (reinterpret_cast<uintptr_t>(sg.dst) & 15) == 0 &&
+                       (sg.src == nullptr || (reinterpret_cast<uintptr_t>(sg.src) & 15) == 0);
+  if (!aligned) {
+    copy_words(sg.dst, sg.src, sg.len, ci);
+    return;
+  }
+  const int64_t start = ci * kChunk;
   const int64_t rem = static_cast<int64_t>(sg.len) - start;
   const int64_t cnt = rem < kChunk ? rem : kChunk;
-  const bool vec = (reinterpret_cast<uintptr_t>(sg.dst) & 15) == 0 &&
-                   (sg.src == nullptr || (reinterpret_cast<uintptr_t>(sg.src) & 15) == 0);
-  copy_chunk(sg.dst + start, sg.src ? sg.src + start : nullptr, cnt, vec);
+  copy_chunk(sg.dst + start, sg.src ? sg.src + start : nullptr, cnt);
 }
 
 // Fans (the all-gather side): the shard pointers once, then up to kMaxFans
@@ -156,6 +283,86 @@ __device__ __forceinline__ int find_fan(const FanList& L, int64_t c) {
   return lo;
 }
 
+// Block ci of a fan piece whose destination is not 16-byte aligned: as
+// copy_words, the destination's whole 16-byte words by word index, each
+// word's 8 sources found from its position -- one shard's contiguous run
+// (aligned words, realigned) unless a rank boundary falls inside the word,
+// which then goes element by element, like the piece's unaligned ends.
+__device__ __forceinline__ void fan_words(const FanList& L, const FanPiece& f, uint32_t ci) {
+  constexpr uint32_t W = static_cast<uint32_t>(kRounds) * kBlock;
+  const uint32_t t = threadIdx.x;
+  const uint32_t len = static_cast<uint32_t>(f.len), chunk = static_cast<uint32_t>(f.chunk);
+  const uint32_t j0 = static_cast<uint32_t>(f.j0);
+  auto src = [&](uint32_t o) {
+    const uint32_t x = j0 + o;
+    const uint32_t q = x / chunk;
+    return L.shard[f.s0 + static_cast<int32_t>(q)] + f.shard_off + (x - q * chunk);
+  };
+  const uint32_t dmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(f.dst) & 15);
+  const uint32_t head0 = ((16 - dmis) & 15) >> 1;
+  const uint32_t head = head0 < len ? head0 : len;
+  const uint32_t words = (len - head) >> 3;
+  const uint32_t tail0 = head + (words << 3);
+  const uint32_t last_ci = (len - 1) / static_cast<uint32_t>(kChunk);
+  const bool in_head = ci == 0 && t < head;
+  const bool in_tail = ci == last_ci && tail0 + t < len;
+  const uint16_t hv = in_head ? *src(t) : 0;
+  const uint16_t tv = in_tail ? *src(tail0 + t) : 0;
+  uint4 x[kRounds];
+  // the block's words [w_lo, w_hi): when they all lie in one rank's chunk
+  // (every block but those at a rank boundary) the shard pointer and the
+  // source's misalignment are block-uniform
+  const uint32_t w_lo = ci * W;
+  const uint32_t w_hi = words < w_lo + W ? words : w_lo + W;
+  uint32_t q_lo = 0, q_hi = 1;
+  if (w_lo < w_hi) {
+    q_lo = (j0 + head + (w_lo << 3)) / chunk;
+    q_hi = (j0 + head + ((w_hi - 1) << 3) + 7) / chunk;
+  }
+  if (q_lo == q_hi) {
+    const uint32_t off_lo = j0 + head + (w_lo << 3) - q_lo * chunk;
+    const uintptr_t p_lo = reinterpret_cast<uintptr_t>(
+        L.shard[f.s0 + static_cast<int32_t>(q_lo)] + f.shard_off + off_lo);
+    const uint32_t sh = static_cast<uint32_t>(p_lo & 15);
+    const uint4* sa = reinterpret_cast<const uint4*>(p_lo - sh);  // word w: sa[w - w_lo]
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const uint32_t i = t + static_cast<uint32_t>(k) * kBlock;
+      if (w_lo + i < w_hi) x[k] = sh == 0 ? sa[i] : realign16(sa[i], sa[i + 1], sh);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const uint32_t w = ci * W + t + static_cast<uint32_t>(k) * kBlock;
+      if (w >= words) continue;
+      const uint32_t o0 = head + (w << 3);
+      const uint32_t x0 = j0 + o0;
+      if (x0 / chunk == (x0 + 7) / chunk) {
+        const uintptr_t p = reinterpret_cast<uintptr_t>(src(o0));
+        const uint32_t sh = static_cast<uint32_t>(p & 15);
+        const uint4* sa = reinterpret_cast<const uint4*>(p - sh);
+        x[k] = sh == 0 ? sa[0] : realign16(sa[0], sa[1], sh);
+      } else {
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = static_cast<uint32_t>(*src(o0 + 2 * e)) |
+                 (static_cast<uint32_t>(*src(o0 + 2 * e + 1)) << 16);
+        x[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+  uint16_t* d = f.dst;
+  uint4* db = reinterpret_cast<uint4*>(d + head);
+  if (in_head) d[t] = hv;
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const uint32_t w = ci * W + t + static_cast<uint32_t>(k) * kBlock;
+    if (w < words) db[w] = x[k];
+  }
+  if (in_tail) d[tail0 + t] = tv;
+}
+
 __global__ void __launch_bounds__(kBlock) fan_copy_kernel(FanList L) {
   // one block per chunk (gridDim.x == L.chunks), XCD-contiguous order
   unsigned b = blockIdx.x;
@@ -163,6 +370,10 @@ __global__ void __launch_bounds__(kBlock) fan_copy_kernel(FanList L) {
   if (b < per * kXcds) b = (b % kXcds) * per + b / kXcds;
   const int64_t c = b;
   const FanPiece f = L.fan[find_fan(L, c)];
+  if ((reinterpret_cast<uintptr_t>(f.dst) & 15) != 0) {
+    fan_words(L, f, static_cast<uint32_t>(c - f.first_chunk));
+    return;
+  }
   const uint32_t start = static_cast<uint32_t>(c - f.first_chunk) * static_cast<uint32_t>(kChunk);
   const uint32_t rem = static_cast<uint32_t>(f.len) - start;
   const uint32_t cnt = rem < static_cast<uint32_t>(kChunk) ? rem : static_cast<uint32_t>(kChunk);
@@ -175,7 +386,7 @@ __global__ void __launch_bounds__(kBlock) fan_copy_kernel(FanList L) {
     // the block's elements lie in one rank's chunk (every block, when chunks
     // are long): one shard pointer for the block, a plain copy
     const uint16_t* s = L.shard[f.s0 + static_cast<int32_t>(q0)] + f.shard_off + (base - q0 * chunk);
-    copy_chunk(d, s, cnt, f.vec != 0);
+    copy_chunk(d, s, cnt);
     return;
   }
   auto src = [&](uint32_t o) {

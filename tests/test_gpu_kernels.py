@@ -383,6 +383,45 @@ def test_pack_ragged(misalign, align):
     assert H.canaries_intact(whole, g)
 
 
+@pytest.mark.parametrize("length", [1, 7, 8, 9, 15, 17, 2040, 2047, 2049, 4103, 20003])
+def test_copy_every_alignment(length):
+    """Pack and unpack of one tensor at every pair of source and destination
+    misalignments (0..7 elements past a 16-byte boundary each): the tensor is
+    a view `o` elements into its buffer, and a k-element tensor ahead of it
+    in the bucket (align 1) puts its flat offset at k.  Lengths straddle the
+    unaligned head, the 8-element words, the tail and the 2048-element chunk.
+    Bit-exact against the oracle's pack, guard bands intact."""
+    import torch
+    for k in range(8):
+        numels = [length, k]  # visited in reverse: the k-element tensor first
+        pl = sbp.bucket_plan(numels, 1 << 30, 1, align=1)
+        opl = OP.bucket_plan(numels, 1 << 30, 1, align=1)
+        assert pl.tensor(0) == (0, k)
+        gh = [synth.normal_bf16(60 + k, synth.tensor_stream(1, 0, 0, t), n, 1e-2)
+              for t, n in enumerate(numels)]
+        want = OS.pack(opl, gh)
+        for o in range(8):
+            base = torch.full((length + o + 24,), 0x5A5A, dtype=torch.int16, device=H.dev())
+            view = base[o:o + length]
+            view.copy_(H.from_np_u16(gh[0]))
+            other = H.from_np_u16(gh[1]) if k else H.empty_u16(0)
+            whole, flat, g = H.guarded(pl.flat_numel, 2)
+            flat.fill_(0x7777)
+            sbp.pack_grads(pl, [view, other], flat)
+            back_base = torch.full((length + o + 24,), 0x5A5A, dtype=torch.int16,
+                                   device=H.dev())
+            back = back_base[o + 1:o + 1 + length]  # another misalignment on the way back
+            other_back = H.empty_u16(k)
+            sbp.unpack_params(pl, flat, [back, other_back])
+            torch.cuda.synchronize()
+            what = f"length {length}, flat offset {k}, view offset {o}"
+            H.assert_bits_equal(H.to_np_u16(flat), want, f"pack ({what})")
+            assert H.canaries_intact(whole, g), what
+            H.assert_bits_equal(H.to_np_u16(back), gh[0], f"unpack ({what})")
+            b = H.to_np_u16(back_base)
+            assert np.all(b[:o + 1] == 0x5A5A) and np.all(b[o + 1 + length:] == 0x5A5A), what
+
+
 def test_pack_one_bucket_at_a_time():
     import torch
     numels = [37, 8, 1, 130, 0, 64, 9, 250, 3, 20000, 8192 * 3 + 1]
