@@ -1271,7 +1271,8 @@ def stream_mix(seed, passes=6, reps=5):
     accumulate and the fused step at several R.  Every configuration is timed
     round-robin in one process (`passes` rounds of `reps` launches each, HIP
     events on the launch stream, median), so all share one placement of the
-    arrays.  Algorithmic bytes per element as in the roofline table."""
+    arrays (a spread arena).  Algorithmic bytes per element as in the
+    roofline table."""
     import statistics as st
     import torch
     import sharded_bucket_plan_amd as sbp
@@ -1280,14 +1281,15 @@ def stream_mix(seed, passes=6, reps=5):
     w = synth.WORKLOADS["llama3_8b"]
     n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
     dev = torch.device("cuda:0")
-    peers = [synth.dev_normal_bf16(torch.empty(n, dtype=torch.int16, device=dev), seed,
+    # every array in one spread arena, as the benchmark's step places them
+    arena = sbp.Arena([2 * n] * 8 + [4 * n] * 5 + [2 * n] * 2)
+    peers = [synth.dev_normal_bf16(arena.tensor(r, torch.int16, n), seed,
                                    synth.peer_stream(1, 0, r), 1e-3) for r in range(8)]
-    f32 = lambda: torch.zeros(n, dtype=torch.float32, device=dev)
-    acc, m, v, out = f32(), f32(), f32(), f32()
-    master = synth.dev_normal_f32(torch.empty(n, dtype=torch.float32, device=dev), seed,
+    acc, m, v, out = (arena.tensor(8 + j, torch.float32, n).zero_() for j in range(4))
+    master = synth.dev_normal_f32(arena.tensor(12, torch.float32, n), seed,
                                   synth.master_stream(0), 0.02)
-    p = torch.empty(n, dtype=torch.int16, device=dev)
-    flat = torch.empty(n, dtype=torch.int16, device=dev)
+    p = arena.tensor(13, torch.int16, n)
+    flat = arena.tensor(14, torch.int16, n)
     one = sbp.bucket_plan([n], 4 * n, 1)  # one tensor, one bucket: pack is a plain copy
     ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=dev)
     sq = torch.empty(1, dtype=torch.float64, device=dev)
