@@ -1100,7 +1100,7 @@ LAYOUT_CALL_BYTES = {
 }
 
 
-def layout_call(seed, workload, plan_kind, call, warmup, steps):
+def layout_call(seed, workload, plan_kind, call, warmup, steps, misalign=0):
     """One layout call made eagerly warmup + steps times on a workload's model,
     nothing else launched on the GPU after the inputs are generated: the run a
     counter pass divides by its number of calls.  Returns the calls made and
@@ -1474,7 +1474,7 @@ def main():
         return
     if args.layout_call:
         print(json.dumps(layout_call(seed, args.workload, args.plan, args.layout_call,
-                                     args.warmup, args.steps)), flush=True)
+                                     args.warmup, args.steps, args.misalign)), flush=True)
         return
     if args.stream_mix:
         print(json.dumps(stream_mix(seed)), flush=True)

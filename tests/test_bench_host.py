@@ -111,3 +111,32 @@ def test_traffic_summary_of_a_layout_call(tmp_path):
     assert "fill_bf16_kernel" not in text
     assert f"source_sha256 (layout.hip and its build flags): " \
            f"{bench.kernel_source_hash(bench.LAYOUT_SRC)}" in text
+
+
+def _undefined_globals(path):
+    """Names that some function of `path` reads as globals although neither the
+    module nor the builtins define them (a stdlib symtable walk)."""
+    import builtins
+    import symtable
+    src = open(path).read()
+    top = symtable.symtable(src, path, "exec")
+    defined = {s.get_name() for s in top.get_symbols()
+               if s.is_assigned() or s.is_imported() or s.is_namespace()}
+    defined |= set(dir(builtins)) | {"__file__", "__name__"}
+    bad = set()
+
+    def walk(t):
+        for child in t.get_children():
+            for sym in child.get_symbols():
+                if sym.is_referenced() and sym.is_global() and sym.get_name() not in defined:
+                    bad.add((child.get_name(), sym.get_name()))
+            walk(child)
+    walk(top)
+    return sorted(bad)
+
+
+def test_no_undefined_names():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for rel in ("bench.py", "sharded_bucket_plan_amd/__init__.py", "__graft_entry__.py",
+                "tests/helpers.py", "tests/oracle_pool.py"):
+        assert _undefined_globals(os.path.join(root, rel)) == [], rel
