@@ -97,7 +97,11 @@ static int read_all(FILE* f, void* dst, size_t bytes) {
     }                                                                        \
   } while (0)
 
-static int run_step(const char* in_path, const char* out_path) {
+/* One fused step on the input file's arrays.  use_arena: every device array
+ * from one spread arena (sbp_arena_create) instead of hipMalloc, and this
+ * rank's squared norm of the step's gradient taken first with the
+ * allocation-free call (appended to the output). */
+static int run_step(const char* in_path, const char* out_path, int use_arena) {
   FILE* f = fopen(in_path, "rb");
   if (!f) return fail("cannot open the input file");
   int64_t n = 0;
@@ -126,25 +130,59 @@ static int run_step(const char* in_path, const char* out_path) {
   fclose(f);
 
   void* d_peer[SBP_MAX_PEERS] = {0};
-  void *d_acc = NULL, *d_master = NULL, *d_m = NULL, *d_v = NULL, *d_param = NULL;
-  for (int32_t r = 0; r < R; ++r) {
-    HIP_OK(hipMalloc(&d_peer[r], nb2));
+  void *d_acc = NULL, *d_master = NULL, *d_m = NULL, *d_v = NULL, *d_param = NULL, *d_sq = NULL;
+  sbp_arena* arena = NULL;
+  if (use_arena) {
+    /* peers, acc (maybe empty), master, m, v, param, the squared norm */
+    int64_t bytes[SBP_MAX_PEERS + 6];
+    void* ptr[SBP_MAX_PEERS + 6];
+    int32_t k = 0;
+    for (int32_t r = 0; r < R; ++r) bytes[k++] = (int64_t)nb2;
+    bytes[k++] = with_acc ? (int64_t)nb4 : 0;
+    bytes[k++] = (int64_t)nb4;
+    bytes[k++] = (int64_t)nb4;
+    bytes[k++] = (int64_t)nb4;
+    bytes[k++] = (int64_t)nb2;
+    bytes[k++] = 8;
+    const sbp_status st = sbp_arena_create(bytes, k, (int64_t)2 << 20, (int64_t)512 << 20, 7,
+                                           ptr, &arena);
+    if (st != SBP_OK) {
+      fprintf(stderr, "abi_c: sbp_arena_create: %d %s\n", st, sbp_last_error());
+      return 1;
+    }
+    for (int32_t r = 0; r < R; ++r) d_peer[r] = ptr[r];
+    d_acc = ptr[R];
+    d_master = ptr[R + 1];
+    d_m = ptr[R + 2];
+    d_v = ptr[R + 3];
+    d_param = ptr[R + 4];
+    d_sq = ptr[R + 5];
+  } else {
+    for (int32_t r = 0; r < R; ++r) HIP_OK(hipMalloc(&d_peer[r], nb2));
+    if (with_acc) HIP_OK(hipMalloc(&d_acc, nb4));
+    HIP_OK(hipMalloc(&d_master, nb4));
+    HIP_OK(hipMalloc(&d_m, nb4));
+    HIP_OK(hipMalloc(&d_v, nb4));
+    HIP_OK(hipMalloc(&d_param, nb2));
+  }
+  for (int32_t r = 0; r < R; ++r)
     HIP_OK(hipMemcpy(d_peer[r], h_peers + nb2 * (size_t)r, nb2, hipMemcpyHostToDevice));
-  }
-  if (with_acc) {
-    HIP_OK(hipMalloc(&d_acc, nb4));
-    HIP_OK(hipMemcpy(d_acc, h_acc, nb4, hipMemcpyHostToDevice));
-  }
-  HIP_OK(hipMalloc(&d_master, nb4));
-  HIP_OK(hipMalloc(&d_m, nb4));
-  HIP_OK(hipMalloc(&d_v, nb4));
-  HIP_OK(hipMalloc(&d_param, nb2));
+  if (with_acc) HIP_OK(hipMemcpy(d_acc, h_acc, nb4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_master, h_state, nb4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_m, h_state + nb4, nb4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_v, h_state + 2 * nb4, nb4, hipMemcpyHostToDevice));
 
   hipStream_t stream;
   HIP_OK(hipStreamCreate(&stream));
+  if (use_arena) {
+    const sbp_status sn = sbp_grad_sq_norm_noalloc((const void* const*)d_peer, R,
+                                                   (const float*)d_acc, scale, n, NULL,
+                                                   (double*)d_sq, stream);
+    if (sn != SBP_OK) {
+      fprintf(stderr, "abi_c: sbp_grad_sq_norm_noalloc: %d %s\n", sn, sbp_last_error());
+      return 1;
+    }
+  }
   const sbp_status st = sbp_adamw_shard((const void* const*)d_peer, R, (const float*)d_acc, scale,
                                         (float*)d_master, (float*)d_m, (float*)d_v, d_param, n,
                                         &hp, stream);
@@ -159,16 +197,27 @@ static int run_step(const char* in_path, const char* out_path) {
   HIP_OK(hipMemcpy(h_state + nb4, d_m, nb4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(h_state + 2 * nb4, d_v, nb4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(h_param, d_param, nb2, hipMemcpyDeviceToHost));
-  for (int32_t r = 0; r < R; ++r) HIP_OK(hipFree(d_peer[r]));
-  if (d_acc) HIP_OK(hipFree(d_acc));
-  HIP_OK(hipFree(d_master));
-  HIP_OK(hipFree(d_m));
-  HIP_OK(hipFree(d_v));
-  HIP_OK(hipFree(d_param));
+  double sq = 0.0;
+  if (use_arena) {
+    HIP_OK(hipMemcpy(&sq, d_sq, 8, hipMemcpyDeviceToHost));
+    const sbp_status sf = sbp_arena_free(arena);
+    if (sf != SBP_OK) {
+      fprintf(stderr, "abi_c: sbp_arena_free: %d %s\n", sf, sbp_last_error());
+      return 1;
+    }
+  } else {
+    for (int32_t r = 0; r < R; ++r) HIP_OK(hipFree(d_peer[r]));
+    if (d_acc) HIP_OK(hipFree(d_acc));
+    HIP_OK(hipFree(d_master));
+    HIP_OK(hipFree(d_m));
+    HIP_OK(hipFree(d_v));
+    HIP_OK(hipFree(d_param));
+  }
 
   FILE* o = fopen(out_path, "wb");
   if (!o) return fail("cannot open the output file");
   if (fwrite(h_state, 1, 3 * nb4 + nb2, o) != 3 * nb4 + nb2) return fail("short write");
+  if (use_arena && fwrite(&sq, 1, 8, o) != 8) return fail("short write");
   fclose(o);
   free(host);
   printf("step %lld done\n", (long long)n);
@@ -178,6 +227,7 @@ static int run_step(const char* in_path, const char* out_path) {
 int main(int argc, char** argv) {
   printf("%s\n", sbp_version());
   if (argc >= 2 && strcmp(argv[1], "plan") == 0) return run_plan(argc, argv);
-  if (argc == 4 && strcmp(argv[1], "step") == 0) return run_step(argv[2], argv[3]);
-  return fail("usage: abi_c plan CAP N ALIGN FLAGS NUMEL... | abi_c step IN OUT");
+  if (argc == 4 && strcmp(argv[1], "step") == 0) return run_step(argv[2], argv[3], 0);
+  if (argc == 4 && strcmp(argv[1], "arena_step") == 0) return run_step(argv[2], argv[3], 1);
+  return fail("usage: abi_c plan CAP N ALIGN FLAGS NUMEL... | abi_c step|arena_step IN OUT");
 }

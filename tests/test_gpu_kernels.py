@@ -869,10 +869,13 @@ def test_graph_capture_replays():
 
 
 @pytest.mark.parametrize("with_acc", [False, True])
-def test_c_client_fused_step(tmp_path, with_acc):
+@pytest.mark.parametrize("mode", ["step", "arena_step"])
+def test_c_client_fused_step(tmp_path, with_acc, mode):
     """A C99 program using only include/sbp.h and the HIP runtime's C API
-    (its own hipMalloc'd buffers and stream, no torch) runs one fused step;
-    its outputs equal the oracle's bit for bit."""
+    (its own buffers and stream, no torch) runs one fused step; its outputs
+    equal the oracle's bit for bit.  "step": buffers from hipMalloc;
+    "arena_step": every buffer from one spread arena, and the gradient's
+    squared norm taken first with the allocation-free call."""
     import struct
     import subprocess
     exe = H.build_c_client(tmp_path)
@@ -891,12 +894,19 @@ def test_c_client_fused_step(tmp_path, with_acc):
         body += acc.tobytes()
     body += th.tobytes() + m.tobytes() + v.tobytes()
     (tmp_path / "in.bin").write_bytes(hdr + body)
-    print(f"c client step n={n} R={R} acc={with_acc}", flush=True)
-    r = subprocess.run([exe, "step", str(tmp_path / "in.bin"), str(tmp_path / "out.bin")],
+    print(f"c client {mode} n={n} R={R} acc={with_acc}", flush=True)
+    r = subprocess.run([exe, mode, str(tmp_path / "in.bin"), str(tmp_path / "out.bin")],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     out = (tmp_path / "out.bin").read_bytes()
-    assert len(out) == 14 * n
+    assert len(out) == 14 * n + (8 if mode == "arena_step" else 0)
+    if mode == "arena_step":
+        S = OS.reduce_peers(peers)
+        G = S if acc is None else OS.accumulate(acc, S)
+        sq = np.frombuffer(out, np.float64, 1, 14 * n)[0]
+        want_sq = OS.grad_sq_norm(G, scale)
+        gpl = H.norm_gpl(R, with_acc)
+        assert abs(sq - want_sq) <= H.sq_norm_bound(G, scale, n, gpl), (sq, want_sq)
     got = (np.frombuffer(out, np.float32, n, 0), np.frombuffer(out, np.float32, n, 4 * n),
            np.frombuffer(out, np.float32, n, 8 * n), np.frombuffer(out, np.uint16, n, 12 * n))
     want = OS.shard_step(peers, acc, scale, th, m, v, HP, t)

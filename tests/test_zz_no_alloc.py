@@ -89,3 +89,41 @@ def test_noalloc_empty_and_refusals():
     assert st == sbp.SBP_ERANGE
     torch.cuda.synchronize()
     assert sq.item() == 0.0  # untouched
+
+
+def test_noalloc_in_a_captured_graph():
+    """What the call is for: captured in a HIP graph with no allocation in or
+    around it.  Four replays, each after eager calls of other sizes that
+    overwrite the shared scratch; every replay's squared norm and G must
+    equal the eager result (each call writes every scratch slot it reads)."""
+    import torch
+    R, n = 4, 256 * 8 * 40 + 3
+    bufs, acc_d, G = _inputs(R, True, n, 77)
+    scale = sbp.mean_scale(R, 2)
+    sq = torch.empty(1, dtype=torch.float64, device=H.dev())
+    g_out = torch.empty(n, dtype=torch.float32, device=H.dev())
+    sbp.grad_sq_norm_noalloc(bufs, acc_d, scale, n, sq, g_sum_out=g_out)  # eager (and first) call
+    torch.cuda.synchronize()
+    want_sq, want_g = sq.clone(), g_out.clone()
+    other_bufs, _, _ = _inputs(8, False, 256 * 8 * 1000 + 1, 78)  # a larger call, other data
+    other_sq = torch.empty(1, dtype=torch.float64, device=H.dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the side stream, as capture expects
+        sbp.grad_sq_norm_noalloc(bufs, acc_d, scale, n, sq, g_sum_out=g_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sbp.grad_sq_norm_noalloc(bufs, acc_d, scale, n, sq, g_sum_out=g_out)
+    for rep in range(4):
+        # eager work between replays: other sizes through the same scratch
+        sbp.grad_sq_norm_noalloc(other_bufs, None, 0.125, 256 * 8 * 1000 + 1, other_sq)
+        sbp.grad_sq_norm_noalloc(bufs[:1], None, 1.0, n, other_sq)
+        sq.fill_(-1.0)
+        g_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sq, want_sq), f"replay {rep}: squared norm differs"
+        assert torch.equal(g_out, want_g), f"replay {rep}: G differs"
