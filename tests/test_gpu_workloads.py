@@ -75,36 +75,40 @@ def test_tiny_mlp_all_steps(s):
             H.assert_bits_equal(a, b, f"tiny_mlp s={s} step {t} {name}")
 
 
-def test_gpt2_small_full():
-    """GPT-2-small ZeRO-2 shard (N=8, R=8, 15.5M elements), two steps, every element."""
+@pytest.mark.parametrize("s", range(8))
+def test_gpt2_small_full(s):
+    """GPT-2-small ZeRO-2 shard (N=8, R=8, 15.5M elements), every shard index:
+    every element after every step -- ten steps (the workloads' AdamW run)
+    for shard 0, two for the others (whose master weights differ)."""
     import torch
     w = synth.WORKLOADS["gpt2_small"]
     hp = _hp(w)
     pl = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
     n = pl.shard_numel
     assert n == 15554976
-    th = synth.normal_f32(SEED, synth.master_stream(0), n, w.master_sigma)
+    th = synth.normal_f32(SEED, synth.master_stream(s), n, w.master_sigma)
     z = np.zeros(n, np.float32)
     dth, dm, dv = H.from_np_f32(th), H.from_np_f32(z), H.from_np_f32(z)
     dp = H.empty_u16(n)
     bufs = None
     want = (th, z, z, None)
-    for t in (1, 2):
+    for t in range(1, (10 if s == 0 else 2) + 1):
         bufs = H.dev_peers(SEED, t, 0, w.R, n, w.grad_sigma, bufs)
         sbp.adamw_shard(bufs, None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
         want = OS.shard_step(H.host_peers(SEED, t, 0, w.R, n, w.grad_sigma), None,
                              OS.mean_scale(w.R), want[0], want[1], want[2], hp, t)
-    torch.cuda.synchronize()
-    got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
-    for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"gpt2_small {name}")
+        torch.cuda.synchronize()
+        got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
+        for a_, b_, name in zip(got, want, ("master", "m", "v", "param")):
+            H.assert_bits_equal(a_, b_, f"gpt2_small shard {s} step {t} {name}")
 
 
-def test_gpt2_small_grouped_full():
+@pytest.mark.parametrize("s", range(8))
+def test_gpt2_small_grouped_full(s):
     """GPT-2-small shard with the usual two parameter groups -- weight decay
     on matrices, none on biases, norm gains and other 1-D tensors -- plus a
-    lower lr on the embeddings (a third group); run table from the plan,
-    two steps, every element."""
+    lower lr on the embeddings (a third group); every shard index (each has
+    its own run table from the plan), two steps, every element."""
     import torch
     w = synth.WORKLOADS["gpt2_small"]
     hp = _hp(w)
@@ -115,7 +119,6 @@ def test_gpt2_small_grouped_full():
     tg = [1 if len(shape) == 1 else (2 if "wte" in name or "wpe" in name else 0)
           for name, shape in w.params]
     assert set(tg) == {0, 1, 2}
-    s = 3
     rs, rg = sbp.group_table(pl, s, tg, H.dev())
     eg = OS.shard_groups(opl, s, tg)
     th = synth.normal_f32(SEED, synth.master_stream(s), n, w.master_sigma)
