@@ -143,12 +143,22 @@ class Workload:
     def _alloc_set(self, i):
         w, n, synth = self.w, self.n, self.synth
         spec = self._arrays()
+        buf = None
         if self.placement == "spread":
-            ar = self.sbp.Arena([k * self.torch.empty(0, dtype=dt).element_size()
-                                 for _, dt, k in spec], seed=0x5EED + i)
-            self.arenas.append(ar)
-            buf = {nm: ar.tensor(j, dt, k) for j, (nm, dt, k) in enumerate(spec)}
-        else:
+            try:
+                ar = self.sbp.Arena([k * self.torch.empty(0, dtype=dt).element_size()
+                                     for _, dt, k in spec], seed=0x5EED + i)
+            except self.sbp.SbpError as e:
+                # no virtual memory management, or no room to spread: the
+                # line then says where its arrays really were
+                if i > 0:
+                    raise
+                log(f"bench: spread arena unavailable ({e}); ordinary torch allocations instead")
+                self.placement = "torch"
+            else:
+                self.arenas.append(ar)
+                buf = {nm: ar.tensor(j, dt, k) for j, (nm, dt, k) in enumerate(spec)}
+        if buf is None:
             buf = {nm: self.torch.empty(k, dtype=dt, device=self.dev) for nm, dt, k in spec}
         s = {}
         s["master"] = synth.dev_normal_f32(buf["master"], self.seed + i, synth.master_stream(0),
