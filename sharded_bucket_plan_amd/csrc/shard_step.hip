@@ -64,15 +64,25 @@
 #ifndef SBP_INFLIGHT_KB
 #define SBP_INFLIGHT_KB 56
 #endif
+// The reduce and accumulate passes (no state arrays) have their own cap.
+#ifndef SBP_REDUCE_INFLIGHT_KB
+#define SBP_REDUCE_INFLIGHT_KB SBP_INFLIGHT_KB
+#endif
 // The squared-norm pass ends every block with a block-wide reduction (a
 // barrier); with one block per CU the CU idles through it, so that pass aims
-// at more loads in flight: two blocks per CU at R = 8 with an accumulator
-// (measured 65% -> 71% of 8 TB/s, 80% without the G write).
+// at more loads in flight: four blocks per CU at R = 8, three with an
+// accumulator (at R = 8 on pages spread over the HBM, 74% -> 78% of 8 TB/s
+// against three blocks; 72.6% -> 73.8% with the G write).
 #ifndef SBP_NORM_INFLIGHT_KB
-#define SBP_NORM_INFLIGHT_KB 80
+#define SBP_NORM_INFLIGHT_KB 112
 #endif
 #ifndef SBP_XCD_CHUNK
 #define SBP_XCD_CHUNK 64
+#endif
+// The fused step's own chunk (its 15 streams per element favour shorter
+// runs per XCD than the reduce and accumulate passes).
+#ifndef SBP_FUSED_XCD_CHUNK
+#define SBP_FUSED_XCD_CHUNK 32
 #endif
 #ifndef SBP_NT_LOAD
 #define SBP_NT_LOAD 0
@@ -196,13 +206,13 @@ __device__ __forceinline__ void group_scalars8(const GroupArgs& ga, int64_t lo, 
   }
 }
 
-// This block's tile in the chunked XCD order.  A bijection on
-// [0, gridDim.x): blocks past the last whole round of 8 chunks keep their
-// own tile.
+// This block's tile in the chunked XCD order (C tiles per chunk).  A
+// bijection on [0, gridDim.x): blocks past the last whole round of 8 chunks
+// keep their own tile.
+template <unsigned C = SBP_XCD_CHUNK>
 __device__ __forceinline__ unsigned my_tile() {
   unsigned b = blockIdx.x;
-  if (SBP_XCD_CHUNK > 0) {
-    constexpr unsigned C = SBP_XCD_CHUNK;
+  if constexpr (C > 0) {
     const unsigned full = gridDim.x / (kXcds * C) * (kXcds * C);
     if (b < full) {
       const unsigned x = b % kXcds, k = b / kXcds;
@@ -216,8 +226,9 @@ __device__ __forceinline__ unsigned my_tile() {
 }
 
 // Group (8 elements) handled by this lane.
+template <unsigned C = SBP_XCD_CHUNK>
 __device__ __forceinline__ int64_t my_group() {
-  return static_cast<int64_t>(my_tile()) * kBlock + threadIdx.x;
+  return static_cast<int64_t>(my_tile<C>()) * kBlock + threadIdx.x;
 }
 
 // Widen peer 0's 8 bf16 values and add peers 1..R-1 in ascending order.
@@ -348,7 +359,7 @@ __device__ __forceinline__ void fused_split_tile(const Peers& P, const float* __
   static_assert(R <= 2, "the split map is for light peer counts");
   const int64_t full = (n >> 3) << 3;  // elements in whole groups of 8
   const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
-  const int64_t tile0 = static_cast<int64_t>(my_tile()) * (kBlock * 8);
+  const int64_t tile0 = static_cast<int64_t>(my_tile<SBP_FUSED_XCD_CHUNK>()) * (kBlock * 8);
   const int64_t e[2] = {tile0 + wv * 512 + ln * 4, tile0 + wv * 512 + 256 + ln * 4};
   // a run of 4 lies wholly inside or outside [0, full): full is a multiple of 8
   const bool ok[2] = {e[0] < full, e[1] < full};
@@ -419,7 +430,7 @@ fused_adamw_kernel(Peers P, const float* __restrict__ acc, float scale,
   if constexpr (!GROUPED && R <= 2) {
     fused_split_tile<R, ACC>(P, acc, scale, master, mom1, mom2, pout, n, s);
   } else {
-    const int64_t gi = my_group();
+    const int64_t gi = my_group<SBP_FUSED_XCD_CHUNK>();
     if (gi < groups) {
       u32x4 w[R > 0 ? R : 1];
       if constexpr (R > 0) load_peers<R>(P, gi, w);
@@ -827,7 +838,8 @@ sbp_status sbp_reduce_shard(const void* const* peers, int32_t R, int64_t n, floa
     if constexpr (RR == 0) {
       return sbp::fail(SBP_EINVAL, "sbp_reduce_shard: R must be >= 1");
     } else {
-      return launch(who, reduce_kernel<RR>, n, 16 * RR, stream, P, scale, out, n);
+      return launch_capped(who, reduce_kernel<RR>, n, 16 * RR, SBP_REDUCE_INFLIGHT_KB, 1, stream, P,
+                           scale, out, n);
     }
   });
 }
@@ -856,9 +868,11 @@ sbp_status sbp_accumulate_grads(float* acc, const void* const* peers, int32_t R,
     if constexpr (RR == 0) {
       return sbp::fail(SBP_EINVAL, "sbp_accumulate_grads: R must be >= 1");
     } else if (first) {
-      return launch(who, accumulate_kernel<RR, true>, n, 16 * RR, stream, P, acc, n);
+      return launch_capped(who, accumulate_kernel<RR, true>, n, 16 * RR, SBP_REDUCE_INFLIGHT_KB, 1,
+                           stream, P, acc, n);
     } else {
-      return launch(who, accumulate_kernel<RR, false>, n, 16 * RR + 32, stream, P, acc, n);
+      return launch_capped(who, accumulate_kernel<RR, false>, n, 16 * RR + 32,
+                           SBP_REDUCE_INFLIGHT_KB, 1, stream, P, acc, n);
     }
   });
 }
