@@ -65,6 +65,12 @@ uint64_t below(uint64_t& s, uint64_t m) {
   return x % m;
 }
 
+// HIP keeps a failed call's error as the thread's last error, where the next
+// unrelated launch check (the library's, or the caller's own) would report
+// it.  The arena reports its failures through its status and message, so it
+// clears that state after a failed call it has handled.
+void clear_hip_error() { (void)hipGetLastError(); }
+
 void release_all(sbp_arena* a, std::vector<hipMemGenericAllocationHandle_t>& loose) {
   for (auto& p : a->mapped) (void)hipMemUnmap(p.first, static_cast<size_t>(p.second));
   a->mapped.clear();
@@ -77,6 +83,7 @@ void release_all(sbp_arena* a, std::vector<hipMemGenericAllocationHandle_t>& loo
       (void)hipMemAddressFree(a->base[i], static_cast<size_t>(a->reserved[i]));
   a->base.clear();
   a->reserved.clear();
+  clear_hip_error();
 }
 
 sbp_status hip_fail(const char* what, hipError_t e) {
@@ -178,7 +185,10 @@ sbp_status sbp_arena_create(const int64_t* bytes, int32_t n_arrays, int64_t chun
     hipMemGenericAllocationHandle_t h;
     e = hipMemCreate(&h, static_cast<size_t>(chunk_bytes), &prop, 0);
     if (e != hipSuccess) {
-      if (k >= need) break;
+      if (k >= need) {  // enough for the arrays: spread over what exists
+        clear_hip_error();
+        break;
+      }
       return bail(hip_fail("hipMemCreate", e));
     }
     loose.push_back(h);

@@ -107,3 +107,29 @@ def test_fused_step_on_arena_arrays_gpt2_small_full():
     got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
     for x, y, name in zip(got, want, ("master", "m", "v", "param")):
         H.assert_bits_equal(x, y, f"gpt2_small on the arena {name}")
+
+
+def test_failed_arena_leaves_no_hip_error():
+    """An arena larger than the whole device fails (out of memory part way
+    through creating its chunks).  The chunks it did create go back, and the
+    HIP error it handled is not left as the thread's last error, where the
+    next launch check (torch's, here) would report it."""
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free0, total = torch.cuda.mem_get_info()
+    with pytest.raises(sbp.SbpError) as err:
+        sbp.Arena([total + (16 << 30)], chunk=64 * MiB)
+    assert err.value.status in (sbp.SBP_ENOMEM, sbp.SBP_EHIP), err.value
+    x = torch.arange(1 << 20, dtype=torch.float64, device=H.dev())
+    assert float(x.sum().item()) == float((1 << 20) * ((1 << 20) - 1) // 2)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 >= free0 - 256 * MiB
+    a = sbp.Arena([4 * MiB], chunk=2 * MiB, spread=64 * MiB)
+    t = a.tensor(0, torch.int32)
+    t.fill_(3)
+    torch.cuda.synchronize()
+    assert int(t.sum().item()) == 3 * t.numel()
