@@ -23,13 +23,15 @@
 //     arguments);
 //   - one pass: one 256-lane block per tile of 2048 elements.  The hardware
 //     hands blocks to the 8 XCDs round-robin; the tiles are dealt back in
-//     chunks of 64 consecutive tiles per XCD (block b, the k-th block of XCD
-//     x = b mod 8, works on tile ((k / 64) * 8 + x) * 64 + k mod 64), so each
-//     XCD sweeps runs of 128K elements while all eight advance together
-//     through every stream.  Measured on MI355X against one contiguous
-//     eighth per XCD: fused step 68.3% -> 70.3% of 8 TB/s, accumulate
-//     67.8% -> 71.0%, norm pass 69.3% -> 75.0%; single tiles round-robin
-//     (the hardware order) are slower than either;
+//     chunks of C consecutive tiles per XCD (block b, the k-th block of XCD
+//     x = b mod 8, works on tile ((k / C) * 8 + x) * C + k mod C), so each
+//     XCD sweeps runs of C * 2048 elements while all eight advance together
+//     through every stream.  C = 64 measured on MI355X against one
+//     contiguous eighth per XCD: fused step 68.3% -> 70.3% of 8 TB/s,
+//     accumulate 67.8% -> 71.0%, norm pass 69.3% -> 75.0%; single tiles
+//     round-robin (the hardware order) are slower than either.  The fused
+//     step gains another 0.2-0.35 points at C = 32, where the reduce and
+//     accumulate passes lose 0.3-1 point, so it has its own C;
 //   - the mix of 11-15 read and write streams runs fastest on MI355X when
 //     each CU keeps about 56 KB of loads in flight; more outstanding
 //     requests congest HBM.  The launch reserves LDS (unused by the kernels)
@@ -680,9 +682,11 @@ sbp_status allow_lds(K kernel, unsigned lds) {
   if (done.count({key, dev})) return SBP_OK;
   hipError_t e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
-  if (e != hipSuccess)
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // reported through the status, not left for the next check
     return sbp::fail(SBP_EHIP,
                      std::string("raising the kernel's LDS limit failed: ") + hipGetErrorString(e));
+  }
   done.insert({key, dev});
   return SBP_OK;
 }
@@ -1164,19 +1168,23 @@ static sbp_status scratch_workspace(double** ws, int64_t need) {
   static double* addr[64] = {};
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess)
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // reported through the status, not left for the next check
     return sbp::fail(SBP_EHIP, std::string("sbp_grad_sq_norm_noalloc: hipGetDevice failed: ") +
                                    hipGetErrorString(e));
+  }
   if (dev < 0 || dev >= 64)
     return sbp::fail(SBP_EINVAL, "sbp_grad_sq_norm_noalloc: device id outside 0..63");
   std::lock_guard<std::mutex> lock(mu);
   if (addr[dev] == nullptr) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || p == nullptr)
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
       return sbp::fail(SBP_EHIP,
                        std::string("sbp_grad_sq_norm_noalloc: looking up the scratch array "
                                    "failed: ") + hipGetErrorString(e));
+    }
     addr[dev] = static_cast<double*>(p);
   }
   *ws = addr[dev];
