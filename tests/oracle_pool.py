@@ -134,6 +134,33 @@ def grouped_state(job):
     return th, m, v, p
 
 
+def clip_norm_partial(job):
+    """This slice's part of the squared norm of g = fl(S * scale), S the R
+    peers' sum at step 1: the oracle's grad_sq_norm (correctly rounded)."""
+    name, seed, i0, i1, scale = job
+    w = synth.WORKLOADS[name]
+    n = i1 - i0
+    peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), n, w.grad_sigma, i0)
+             for r in range(w.R)]
+    return job, OS.grad_sq_norm(OS.reduce_peers(peers), np.float32(scale))
+
+
+def clipped_state(job):
+    """The oracle's state for [i0, i1) after one clipped step taken the way
+    the benchmark's --clip step takes it: the peers' sum G stored, then the
+    update from G alone (no peers, G as the accumulator) with the clipped
+    scale cs."""
+    name, seed, i0, i1, cs = job
+    w = synth.WORKLOADS[name]
+    n = i1 - i0
+    peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), n, w.grad_sigma, i0)
+             for r in range(w.R)]
+    G = OS.reduce_peers(peers)
+    th = synth.normal_f32(seed, synth.master_stream(0), n, w.master_sigma, i0)
+    z = np.zeros(n, np.float32)
+    return OS.shard_step([], G, np.float32(cs), th, z, z, w.adamw, 1)
+
+
 def digests(arrays):
     import xxhash
     return tuple(xxhash.xxh3_128_digest(np.ascontiguousarray(x).view(np.uint8)) for x in arrays)
@@ -149,6 +176,10 @@ def dp_digests(job):
 
 def grouped_digests(job):
     return job, digests(grouped_state(job))
+
+
+def clipped_digests(job):
+    return job, digests(clipped_state(job))
 
 
 def workers():

@@ -185,16 +185,20 @@ def _compare_slices(results, arrays, recompute, what, every=8):
     return done
 
 
-def _arena_state(n, R, K=1, with_acc=False):
+def _arena_state(n, R, K=1, with_acc=False, with_g=False):
     """The step's arrays in one spread arena, as bench.py places them:
-    master, m, v, param shard, then K microbatches of R peers (+ acc)."""
+    master, m, v, param shard, then K microbatches of R peers (+ acc, + the
+    stored G of a clipped step)."""
     import torch
-    sizes = [4 * n] * 3 + [2 * n] + [2 * n] * (R * K) + ([4 * n] if with_acc else [])
+    sizes = ([4 * n] * 3 + [2 * n] + [2 * n] * (R * K) + ([4 * n] if with_acc else [])
+             + ([4 * n] if with_g else []))
     a = sbp.Arena(sizes)
     th, m, v = (a.tensor(j, torch.float32, n) for j in range(3))
     p = a.tensor(3, torch.int16, n)
     mb = [[a.tensor(4 + k * R + r, torch.int16, n) for r in range(R)] for k in range(K)]
     acc = a.tensor(4 + R * K, torch.float32, n) if with_acc else None
+    if with_g:
+        return a, th, m, v, p, mb, acc, a.tensor(len(sizes) - 1, torch.float32, n)
     return a, th, m, v, p, mb, acc
 
 
@@ -224,6 +228,51 @@ def test_llama3_8b_shard_full():
         print(f"llama3_8b: GPU steps done; comparing {len(jobs)} slices", flush=True)
         done = _compare_slices(results, (dth, dm, dv, dp),
                                lambda job: OPL.shard_state(job), "llama3_8b")
+    assert done == len(jobs)
+
+
+def test_llama3_8b_clipped_full():
+    """The Llama-3-8B shard with global-norm clipping as bench.py --clip 1.0
+    takes it: the norm pass writes G and this rank's float64 squared norm,
+    the clip coefficient folds into the scale, and the update reads G alone.
+    The squared norm is checked against the oracle's (per-slice correctly
+    rounded sums, then their correctly rounded sum) within the fixed tree's
+    derived bound, the clipped scale must be the oracle's, and every element
+    of the updated state against the oracle's clipped step, slice by slice."""
+    import math
+    from tests import oracle_pool as OPL
+    import torch
+    w = synth.WORKLOADS["llama3_8b"]
+    hp = _hp(w)
+    n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
+    scale = sbp.mean_scale(w.R)
+    max_norm = 1.0
+    spans = [(i0, min(n, i0 + OPL.SLICE)) for i0 in range(0, n, OPL.SLICE)]
+    with OPL.pool() as pool:
+        parts = pool.imap(OPL.clip_norm_partial,
+                          [("llama3_8b", SEED, i0, i1, scale) for i0, i1 in spans])
+        arena, dth, dm, dv, dp, mb, _, dg = _arena_state(n, w.R, with_g=True)
+        synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
+        dm.zero_()
+        dv.zero_()
+        H.dev_peers(SEED, 1, 0, w.R, n, w.grad_sigma, mb[0])
+        sq = sbp.grad_sq_norm(mb[0], None, scale, n, g_sum_out=dg).item()
+        cs, coef = sbp.clip_scale(sq, max_norm, scale)
+        sbp.adamw_shard([], dg, cs, dth, dm, dv, dp, hp, 1)
+        torch.cuda.synchronize()
+        want_total = math.fsum(p for _, p in parts)
+        u = 2.0 ** -53
+        d = H.sq_norm_depth(n, H.norm_gpl(w.R, False))
+        bound = (d * u / (1 - d * u) + 2 * u) * want_total * (1 + 1e-9)
+        assert abs(sq - want_total) <= bound, (sq, want_total, bound)
+        want_cs = OS.clipped_scale(OS.mean_scale(w.R), OS.clip_coef(want_total, max_norm))
+        assert cs == float(want_cs), (cs, float(want_cs))
+        assert coef < 1.0  # clipping is active at this max_norm
+        print(f"llama3_8b clipped: norm {math.sqrt(sq):.6g}, coefficient {coef:.6g}; "
+              f"comparing {len(spans)} slices", flush=True)
+        jobs = [("llama3_8b", SEED, i0, i1, cs) for i0, i1 in spans]
+        done = _compare_slices(pool.imap(OPL.clipped_digests, jobs), (dth, dm, dv, dp),
+                               lambda job: OPL.clipped_state(job), "llama3_8b clipped")
     assert done == len(jobs)
 
 
