@@ -134,28 +134,42 @@ def grouped_state(job):
     return th, m, v, p
 
 
+def _step1_scale(w, seed):
+    """The oracle's normalisation of step 1: 1/C over the ranks' valid-token
+    counts, or the mean 1/(R*K)."""
+    if w.norm == "tokens":
+        return OS.tokens_scale([synth.tokens(seed, 1, r) for r in range(w.R)])
+    return OS.mean_scale(w.R, w.K)
+
+
+def _step1_g(w, seed, i0, i1):
+    """G of step 1 over [i0, i1): the first K - 1 microbatches' peer sums
+    accumulated, plus the last one's (the sum the norm pass stores)."""
+    A = None
+    for k in range(w.K):
+        peers = [synth.normal_bf16(seed, synth.peer_stream(1, k, r), i1 - i0, w.grad_sigma, i0)
+                 for r in range(w.R)]
+        A = OS.accumulate(A, OS.reduce_peers(peers))
+    return A
+
+
 def clip_norm_partial(job):
-    """This slice's part of the squared norm of g = fl(S * scale), S the R
-    peers' sum at step 1: the oracle's grad_sq_norm (correctly rounded)."""
-    name, seed, i0, i1, scale = job
+    """This slice's part of the squared norm of g = fl(G * scale) at step 1:
+    the oracle's grad_sq_norm (correctly rounded)."""
+    name, seed, i0, i1 = job
     w = synth.WORKLOADS[name]
-    n = i1 - i0
-    peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), n, w.grad_sigma, i0)
-             for r in range(w.R)]
-    return job, OS.grad_sq_norm(OS.reduce_peers(peers), np.float32(scale))
+    return job, OS.grad_sq_norm(_step1_g(w, seed, i0, i1), _step1_scale(w, seed))
 
 
 def clipped_state(job):
     """The oracle's state for [i0, i1) after one clipped step taken the way
-    the benchmark's --clip step takes it: the peers' sum G stored, then the
+    the benchmark's --clip step takes it: G stored by the norm pass, then the
     update from G alone (no peers, G as the accumulator) with the clipped
-    scale cs."""
+    scale cs (the oracle's)."""
     name, seed, i0, i1, cs = job
     w = synth.WORKLOADS[name]
     n = i1 - i0
-    peers = [synth.normal_bf16(seed, synth.peer_stream(1, 0, r), n, w.grad_sigma, i0)
-             for r in range(w.R)]
-    G = OS.reduce_peers(peers)
+    G = _step1_g(w, seed, i0, i1)
     th = synth.normal_f32(seed, synth.master_stream(0), n, w.master_sigma, i0)
     z = np.zeros(n, np.float32)
     return OS.shard_step([], G, np.float32(cs), th, z, z, w.adamw, 1)

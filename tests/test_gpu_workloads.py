@@ -231,49 +231,75 @@ def test_llama3_8b_shard_full():
     assert done == len(jobs)
 
 
-def test_llama3_8b_clipped_full():
-    """The Llama-3-8B shard with global-norm clipping as bench.py --clip 1.0
-    takes it: the norm pass writes G and this rank's float64 squared norm,
-    the clip coefficient folds into the scale, and the update reads G alone.
-    The squared norm is checked against the oracle's (per-slice correctly
-    rounded sums, then their correctly rounded sum) within the fixed tree's
-    derived bound, the clipped scale must be the oracle's, and every element
-    of the updated state against the oracle's clipped step, slice by slice."""
+def _clipped_full(name, max_norm, slice_len):
+    """One clipped step of workload `name` at full size, as bench.py --clip
+    takes it: the first K - 1 microbatches accumulated over the whole shard,
+    the norm pass over the accumulator and the last microbatch writing G and
+    this rank's float64 squared norm, the clip coefficient folded into the
+    scale, and the update reading G alone.  The squared norm is checked
+    against the oracle's (per-slice correctly rounded sums, then their
+    correctly rounded sum) within the fixed tree's derived bound plus that
+    extra rounding, the clipped scale must be the oracle's, and every element
+    of the updated state is compared with the oracle's clipped step, slice by
+    slice on the host's cores.  Returns the clip coefficient."""
     import math
     from tests import oracle_pool as OPL
     import torch
-    w = synth.WORKLOADS["llama3_8b"]
+    w = synth.WORKLOADS[name]
     hp = _hp(w)
     n = sbp.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n).shard_numel
-    scale = sbp.mean_scale(w.R)
-    max_norm = 1.0
-    spans = [(i0, min(n, i0 + OPL.SLICE)) for i0 in range(0, n, OPL.SLICE)]
+    accum = w.K > 1
+    spans = [(i0, min(n, i0 + slice_len)) for i0 in range(0, n, slice_len)]
     with OPL.pool() as pool:
-        parts = pool.imap(OPL.clip_norm_partial,
-                          [("llama3_8b", SEED, i0, i1, scale) for i0, i1 in spans])
-        arena, dth, dm, dv, dp, mb, _, dg = _arena_state(n, w.R, with_g=True)
+        parts = pool.imap(OPL.clip_norm_partial, [(name, SEED, i0, i1) for i0, i1 in spans])
+        arena, dth, dm, dv, dp, mb, acc, dg = _arena_state(n, w.R, w.K, with_acc=accum,
+                                                             with_g=True)
         synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
         dm.zero_()
         dv.zero_()
-        H.dev_peers(SEED, 1, 0, w.R, n, w.grad_sigma, mb[0])
-        sq = sbp.grad_sq_norm(mb[0], None, scale, n, g_sum_out=dg).item()
+        if w.norm == "tokens":
+            scale = sbp.tokens_scale([synth.tokens(SEED, 1, r) for r in range(w.R)])
+        else:
+            scale = sbp.mean_scale(w.R, w.K)
+        for k in range(w.K):
+            H.dev_peers(SEED, 1, k, w.R, n, w.grad_sigma, mb[k])
+            if k < w.K - 1:
+                sbp.accumulate_grads(acc, mb[k], first=(k == 0))
+        sq = sbp.grad_sq_norm(mb[w.K - 1], acc, scale, n, g_sum_out=dg).item()
         cs, coef = sbp.clip_scale(sq, max_norm, scale)
         sbp.adamw_shard([], dg, cs, dth, dm, dv, dp, hp, 1)
         torch.cuda.synchronize()
         want_total = math.fsum(p for _, p in parts)
         u = 2.0 ** -53
-        d = H.sq_norm_depth(n, H.norm_gpl(w.R, False))
+        d = H.sq_norm_depth(n, H.norm_gpl(w.R, accum))
         bound = (d * u / (1 - d * u) + 2 * u) * want_total * (1 + 1e-9)
         assert abs(sq - want_total) <= bound, (sq, want_total, bound)
-        want_cs = OS.clipped_scale(OS.mean_scale(w.R), OS.clip_coef(want_total, max_norm))
-        assert cs == float(want_cs), (cs, float(want_cs))
-        assert coef < 1.0  # clipping is active at this max_norm
-        print(f"llama3_8b clipped: norm {math.sqrt(sq):.6g}, coefficient {coef:.6g}; "
+        want_cs = float(OS.clipped_scale(OPL._step1_scale(w, SEED),
+                                         OS.clip_coef(want_total, max_norm)))
+        assert cs == want_cs, (cs, want_cs)
+        print(f"{name} clipped: norm {math.sqrt(sq):.6g}, coefficient {coef:.6g}; "
               f"comparing {len(spans)} slices", flush=True)
-        jobs = [("llama3_8b", SEED, i0, i1, cs) for i0, i1 in spans]
+        jobs = [(name, SEED, i0, i1, want_cs) for i0, i1 in spans]
         done = _compare_slices(pool.imap(OPL.clipped_digests, jobs), (dth, dm, dv, dp),
-                               lambda job: OPL.clipped_state(job), "llama3_8b clipped")
+                               lambda job: OPL.clipped_state(job), f"{name} clipped")
     assert done == len(jobs)
+    return coef
+
+
+def test_llama3_8b_clipped_full():
+    """The Llama-3-8B shard (R = 8, 1,003,782,656 elements) clipped at
+    max_norm 1.0 (bench.py --clip 1.0): every element against the oracle."""
+    from tests import oracle_pool as OPL
+    assert _clipped_full("llama3_8b", 1.0, OPL.SLICE) < 1.0  # clipping is active
+
+
+def test_gpt_7b5_clipped_full():
+    """The '7.5B' shard (R = 8, K = 4, 1/C, 103,890,048 elements) clipped: the
+    norm pass reads the accumulator of three microbatches and the last one's
+    peers.  max_norm 1e-3 (this shard's norm is about 3e-3, so bench.py's
+    1.0 would not clip): every element against the oracle."""
+    from tests import oracle_pool as OPL
+    assert _clipped_full("gpt_7b5", 1e-3, OPL.SLICE // 4) < 1.0
 
 
 def test_llama3_8b_grouped_full():
