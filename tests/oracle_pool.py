@@ -72,20 +72,38 @@ def dp_rank0_packed(seed, plan, numels, grad_sigma, a, b, t=1):
 _DP_PLAN = {}
 
 
-def dp_state(job):
-    """The oracle's state for flat positions [a, b) of the DP replica (N = 1,
-    R = 2) after one step, and rank 0's packed gradient there: rank 0's
-    per-tensor gradients packed, rank 1's bucket-layout gradient, MEAN 1/2."""
-    name, seed, a, b = job
+def _dp_peers(name, seed, a, b):
+    """The DP replica's two contributions over flat positions [a, b): rank
+    0's per-tensor gradients packed, and rank 1's bucket-layout gradient."""
     w = synth.WORKLOADS[name]
     if name not in _DP_PLAN:
         _DP_PLAN[name] = OP.bucket_plan(w.numels, w.bucket_cap_bytes, w.world_n)
-    plan = _DP_PLAN[name]
-    p0 = dp_rank0_packed(seed, plan, w.numels, w.grad_sigma, a, b)
+    p0 = dp_rank0_packed(seed, _DP_PLAN[name], w.numels, w.grad_sigma, a, b)
     p1 = synth.normal_bf16(seed, synth.peer_stream(1, 0, 1), b - a, w.grad_sigma, a)
+    return p0, p1
+
+
+def dp_state(job):
+    """The oracle's state for flat positions [a, b) of the DP replica (N = 1,
+    R = 2) after one step, and rank 0's packed gradient there.  The scale is
+    MEAN 1/2, or the clipped scale given as a fifth job entry (the step then
+    sums the peers again, as a norm pass that stores no G leaves it)."""
+    name, seed, a, b = job[:4]
+    w = synth.WORKLOADS[name]
+    p0, p1 = _dp_peers(name, seed, a, b)
+    scale = OS.mean_scale(w.R) if len(job) == 4 else np.float32(job[4])
     th = synth.normal_f32(seed, synth.master_stream(0), b - a, w.master_sigma, a)
     z = np.zeros(b - a, np.float32)
-    return OS.shard_step([p0, p1], None, OS.mean_scale(w.R), th, z, z, w.adamw, 1) + (p0,)
+    return OS.shard_step([p0, p1], None, scale, th, z, z, w.adamw, 1) + (p0,)
+
+
+def dp_norm_partial(job):
+    """The DP replica's part of the squared norm over [a, b) (MEAN 1/2): the
+    oracle's grad_sq_norm, correctly rounded."""
+    name, seed, a, b = job
+    w = synth.WORKLOADS[name]
+    return job, OS.grad_sq_norm(OS.reduce_peers(list(_dp_peers(name, seed, a, b))),
+                                OS.mean_scale(w.R))
 
 
 _SHARD_MAP = {}

@@ -376,14 +376,17 @@ def test_gpt_7b5_accumulate_tokens_full():
     assert done == len(jobs)
 
 
-def test_llama3_8b_dp_pack_and_step_full():
+def _dp_full(max_norm=None):
     """Llama-3-8B as a full DP replica (N=1, R=2, 8.03B elements): rank 0's
     291 per-tensor gradients packed into the 162 buckets, rank 1's
-    bucket-layout gradient as the other contribution, one fused step.  Every
-    element of every bucket (the packed gradient, master, m, v and the bf16
-    parameters) against the oracle run slice by slice on the host's cores;
-    the first, the last and the largest bucket and 8 seeded random others
-    are compared first."""
+    bucket-layout gradient as the other contribution, one fused step -- with
+    max_norm, clipped as bench.py --clip --clip-recompute takes it (the norm
+    pass reads the two contributions and stores nothing; the fused step sums
+    them again under the clipped scale).  Every element of every bucket (the
+    packed gradient, master, m, v and the bf16 parameters) against the oracle
+    run slice by slice on the host's cores; the first, the last and the
+    largest bucket and 8 seeded random others are compared first."""
+    import math
     from tests import oracle_pool as OPL
     import torch
     w = synth.WORKLOADS["llama3_8b_dp"]
@@ -397,14 +400,19 @@ def test_llama3_8b_dp_pack_and_step_full():
     rng = np.random.default_rng(11)
     others = [b for b in range(B) if b not in (0, B - 1, largest)]
     chosen = sorted({0, B - 1, largest} | set(int(x) for x in rng.choice(others, 8, replace=False)))
-    jobs = []
+    spans = []
     for b in chosen + [b for b in range(B) if b not in chosen]:
         o, c = info[b]["shard_offset"], info[b]["chunk"]
-        jobs += [("llama3_8b_dp", SEED, i0, min(o + c, i0 + OPL.SLICE))
-                 for i0 in range(o, o + c, OPL.SLICE)]
+        spans += [(i0, min(o + c, i0 + OPL.SLICE)) for i0 in range(o, o + c, OPL.SLICE)]
+    what = "llama3_8b_dp" + (" clipped" if max_norm else "")
     t = 1
     with OPL.pool() as pool:
-        results = pool.imap(OPL.dp_digests, jobs)
+        if max_norm:
+            parts = pool.imap(OPL.dp_norm_partial,
+                              [("llama3_8b_dp", SEED, i0, i1) for i0, i1 in spans])
+        else:
+            jobs = [("llama3_8b_dp", SEED, i0, i1) for i0, i1 in spans]
+            results = pool.imap(OPL.dp_digests, jobs)
         sizes = [4 * n] * 3 + [2 * n] * 3  # master, m, v, param, rank 0 flat, rank 1
         arena = sbp.Arena(sizes)
         dth, dm, dv = (arena.tensor(j, torch.float32, n) for j in range(3))
@@ -420,9 +428,26 @@ def test_llama3_8b_dp_pack_and_step_full():
         synth.dev_normal_f32(dth, SEED, synth.master_stream(0), w.master_sigma)
         dm.zero_()
         dv.zero_()
-        sbp.adamw_shard([flat0, peer1], None, sbp.mean_scale(w.R), dth, dm, dv, dp, hp, t)
+        scale = sbp.mean_scale(w.R)
+        if max_norm:
+            sq = sbp.grad_sq_norm([flat0, peer1], None, scale, n).item()
+            scale, coef = sbp.clip_scale(sq, max_norm, scale)
+        sbp.adamw_shard([flat0, peer1], None, scale, dth, dm, dv, dp, hp, t)
         torch.cuda.synchronize()
-        print(f"llama3_8b_dp: GPU step done; comparing all {B} buckets ({chosen} first) in "
+        if max_norm:
+            want_total = math.fsum(p for _, p in parts)
+            u = 2.0 ** -53
+            d = H.sq_norm_depth(n, H.norm_gpl(w.R, False))
+            bound = (d * u / (1 - d * u) + 2 * u) * want_total * (1 + 1e-9)
+            assert abs(sq - want_total) <= bound, (sq, want_total, bound)
+            want_cs = float(OS.clipped_scale(OS.mean_scale(w.R),
+                                             OS.clip_coef(want_total, max_norm)))
+            assert scale == want_cs, (scale, want_cs)
+            assert coef < 1.0
+            print(f"{what}: norm {math.sqrt(sq):.6g}, coefficient {coef:.6g}", flush=True)
+            jobs = [("llama3_8b_dp", SEED, i0, i1, want_cs) for i0, i1 in spans]
+            results = pool.imap(OPL.dp_digests, jobs)
+        print(f"{what}: GPU step done; comparing all {B} buckets ({chosen} first) in "
               f"{len(jobs)} slices", flush=True)
         done = 0
         for job, want in results:
@@ -432,13 +457,25 @@ def test_llama3_8b_dp_pack_and_step_full():
             if OPL.digests(got) != want:
                 exp = OPL.dp_state(job)
                 for x, y, name in zip(got, exp, ("master", "m", "v", "param", "packed rank 0")):
-                    H.assert_bits_equal(x, y, f"llama3_8b_dp {name} in [{i0}, {i1})")
-                raise AssertionError(f"llama3_8b_dp: digests of [{i0}, {i1}) differ")
+                    H.assert_bits_equal(x, y, f"{what} {name} in [{i0}, {i1})")
+                raise AssertionError(f"{what}: digests of [{i0}, {i1}) differ")
             done += 1
             if done % 32 == 0:
-                print(f"llama3_8b_dp: {done} slices equal (through element {i1})", flush=True)
+                print(f"{what}: {done} slices equal (through element {i1})", flush=True)
     assert done == len(jobs)
     assert sum(j[3] - j[2] for j in jobs) == n
+
+
+def test_llama3_8b_dp_pack_and_step_full():
+    """The DP replica's pack and fused step, every element."""
+    _dp_full()
+
+
+def test_llama3_8b_dp_clip_recompute_full():
+    """The DP replica clipped at max_norm 1.0 without a stored G: the norm
+    pass over 8.03B elements (positions beyond 2^32, two groups of 8 per
+    lane), then the fused step from the two contributions; every element."""
+    _dp_full(max_norm=1.0)
 
 
 @pytest.mark.parametrize("kind", ["whole", "per_tensor"])
