@@ -231,12 +231,14 @@ def test_llama3_8b_shard_full():
     assert done == len(jobs)
 
 
-def _clipped_full(name, max_norm, slice_len):
+def _clipped_full(name, max_norm, slice_len, recompute=False):
     """One clipped step of workload `name` at full size, as bench.py --clip
     takes it: the first K - 1 microbatches accumulated over the whole shard,
     the norm pass over the accumulator and the last microbatch writing G and
     this rank's float64 squared norm, the clip coefficient folded into the
-    scale, and the update reading G alone.  The squared norm is checked
+    scale, and the update reading G alone (recompute: as --clip-recompute
+    takes it, the norm pass stores no G and the fused step sums the peers and
+    the accumulator again, which gives the same bits).  The squared norm is checked
     against the oracle's (per-slice correctly rounded sums, then their
     correctly rounded sum) within the fixed tree's derived bound plus that
     extra rounding, the clipped scale must be the oracle's, and every element
@@ -265,9 +267,13 @@ def _clipped_full(name, max_norm, slice_len):
             H.dev_peers(SEED, 1, k, w.R, n, w.grad_sigma, mb[k])
             if k < w.K - 1:
                 sbp.accumulate_grads(acc, mb[k], first=(k == 0))
-        sq = sbp.grad_sq_norm(mb[w.K - 1], acc, scale, n, g_sum_out=dg).item()
+        sq = sbp.grad_sq_norm(mb[w.K - 1], acc, scale, n,
+                              g_sum_out=None if recompute else dg).item()
         cs, coef = sbp.clip_scale(sq, max_norm, scale)
-        sbp.adamw_shard([], dg, cs, dth, dm, dv, dp, hp, 1)
+        if recompute:
+            sbp.adamw_shard(mb[w.K - 1], acc, cs, dth, dm, dv, dp, hp, 1)
+        else:
+            sbp.adamw_shard([], dg, cs, dth, dm, dv, dp, hp, 1)
         torch.cuda.synchronize()
         want_total = math.fsum(p for _, p in parts)
         u = 2.0 ** -53
@@ -291,6 +297,14 @@ def test_llama3_8b_clipped_full():
     max_norm 1.0 (bench.py --clip 1.0): every element against the oracle."""
     from tests import oracle_pool as OPL
     assert _clipped_full("llama3_8b", 1.0, OPL.SLICE) < 1.0  # clipping is active
+
+
+def test_llama3_8b_clipped_recompute_full():
+    """The same clipped Llama step as --clip 1.0 --clip-recompute takes it:
+    the norm pass reads the 8 peers only, then the fused step from the peers
+    under the clipped scale; every element against the oracle."""
+    from tests import oracle_pool as OPL
+    assert _clipped_full("llama3_8b", 1.0, OPL.SLICE, recompute=True) < 1.0
 
 
 def test_gpt_7b5_clipped_full():
