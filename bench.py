@@ -772,6 +772,12 @@ def _probe_lib():
                                        ctypes.c_uint, ctypes.c_void_p]
     L.sbp_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                  ctypes.c_uint, ctypes.c_void_p]
+    L.sbp_probe_streams.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_void_p),
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_uint32, ctypes.c_int, ctypes.c_uint,
+                                    ctypes.c_void_p]
     return L
 
 
@@ -1274,15 +1280,19 @@ def layout_moves(seed, workload="llama3_8b", plan_kind="whole", reps=5, misalign
             "buckets": pl.num_buckets}
 
 
-def stream_mix(seed, passes=6, reps=5):
+def stream_mix(seed, passes=4, reps=5):
     """Achieved HBM bandwidth of the library's own kernels against their mix of
     read and write streams, on the Llama-3-8B shard (n = 1,003,782,656): the
     squared-norm pass (reads only), one-tensor pack (a plain copy), reduce,
-    accumulate and the fused step at several R.  Every configuration is timed
-    round-robin in one process (`passes` rounds of `reps` launches each, HIP
-    events on the launch stream, median), so all share one placement of the
-    arrays (a spread arena).  Algorithmic bytes per element as in the
-    roofline table."""
+    accumulate and the fused step at several R.  Beside each kernel, the
+    ceiling of its own mix: the best of zero-arithmetic passes of exactly its
+    traffic (libsbp_probe.so's sbp_probe_streams, mask 0) over 1 to 4 groups
+    of 8 per lane, 1 to 4 blocks per CU or no cap, and tiles dealt to the XCDs
+    in chunks of 32 or 64.  Every configuration is timed round-robin in one
+    process (`passes` rounds of `reps` launches each, HIP events on the launch
+    stream, median), so all share one placement of the arrays (a spread
+    arena).  Algorithmic bytes per element as in the roofline table."""
+    import ctypes
     import statistics as st
     import torch
     import sharded_bucket_plan_amd as sbp
@@ -1303,8 +1313,11 @@ def stream_mix(seed, passes=6, reps=5):
     one = sbp.bucket_plan([n], 4 * n, 1)  # one tensor, one bucket: pack is a plain copy
     ws = torch.empty(sbp.grad_sq_norm_workspace(n), dtype=torch.float64, device=dev)
     sq = torch.empty(1, dtype=torch.float64, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = sbp.AdamW()
     t = [0]
+    L = _probe_lib()
+    stream = torch.cuda.current_stream()
 
     def fused(R, with_acc):
         def f():
@@ -1312,55 +1325,109 @@ def stream_mix(seed, passes=6, reps=5):
             sbp.adamw_shard(peers[:R], acc if with_acc else None, 0.125, master, m, v, p, hp, t[0])
         return f
 
-    # (name, read streams, write streams, bytes per element, call)
+    def probe(shape, b, f, g, o, gpl, bpc, C):
+        """One zero-arithmetic pass of `shape` = (RB, RF, WF, WG, WB) on the
+        given arrays; returns (call, elements it covers)."""
+        tiles = n // (2048 * gpl)
+        sh = (ctypes.c_int * 5)(*shape)
+        bp = (ctypes.c_void_p * 8)(*[x.data_ptr() for x in b])
+        fp = (ctypes.c_void_p * 4)(*[x.data_ptr() for x in f])
+        args = (sh, gpl, bp, fp, g.data_ptr() if g is not None else None,
+                o.data_ptr() if o is not None else None, sink.data_ptr(), tiles, 0, bpc, C)
+
+        def call():
+            if L.sbp_probe_streams(*args, ctypes.c_void_p(stream.cuda_stream)) != 0:
+                raise RuntimeError(f"sbp_probe_streams failed for {shape}")
+        return call, tiles * 2048 * gpl
+
+    # (name, read streams, write streams, bytes per element, call,
+    #  probe shape (RB, RF, WF, WG, WB), its bf16 / fp32 / G / bf16-out arrays)
     kinds = [
         ("squared norm, R=1", 1, 0, 2, lambda: sbp.grad_sq_norm(peers[:1], None, 1.0, n,
-                                                                workspace=ws, sq_out=sq)),
+                                                                workspace=ws, sq_out=sq),
+         (1, 0, 0, 0, 0), peers[:1], [], None, None),
         ("squared norm, R=2", 2, 0, 4, lambda: sbp.grad_sq_norm(peers[:2], None, 0.5, n,
-                                                                workspace=ws, sq_out=sq)),
+                                                                workspace=ws, sq_out=sq),
+         (2, 0, 0, 0, 0), peers[:2], [], None, None),
         ("squared norm of the accumulator (R=0)", 1, 0, 4,
-         lambda: sbp.grad_sq_norm([], acc, 0.125, n, workspace=ws, sq_out=sq)),
+         lambda: sbp.grad_sq_norm([], acc, 0.125, n, workspace=ws, sq_out=sq),
+         (0, 1, 0, 0, 0), [], [acc], None, None),
         ("squared norm, R=8", 8, 0, 16, lambda: sbp.grad_sq_norm(peers, None, 0.125, n,
-                                                                 workspace=ws, sq_out=sq)),
+                                                                 workspace=ws, sq_out=sq),
+         (8, 0, 0, 0, 0), peers, [], None, None),
         ("squared norm, R=8 + accumulator", 9, 0, 20,
-         lambda: sbp.grad_sq_norm(peers, acc, 0.125, n, workspace=ws, sq_out=sq)),
-        ("pack of one tensor (copy)", 1, 1, 4, lambda: sbp.pack_grads(one, [peers[0]], flat)),
-        ("reduce, R=1", 1, 1, 6, lambda: sbp.reduce_shard(peers[:1], 1.0, out)),
-        ("reduce, R=8", 8, 1, 20, lambda: sbp.reduce_shard(peers, 0.125, out)),
+         lambda: sbp.grad_sq_norm(peers, acc, 0.125, n, workspace=ws, sq_out=sq),
+         (8, 1, 0, 0, 0), peers, [acc], None, None),
+        ("pack of one tensor (copy)", 1, 1, 4, lambda: sbp.pack_grads(one, [peers[0]], flat),
+         (1, 0, 0, 0, 1), peers[:1], [], None, flat),
+        ("reduce, R=1", 1, 1, 6, lambda: sbp.reduce_shard(peers[:1], 1.0, out),
+         (1, 0, 0, 1, 0), peers[:1], [], out, None),
+        ("reduce, R=8", 8, 1, 20, lambda: sbp.reduce_shard(peers, 0.125, out),
+         (8, 0, 0, 1, 0), peers, [], out, None),
         ("squared norm, R=8, writing G", 8, 1, 20,
-         lambda: sbp.grad_sq_norm(peers, None, 0.125, n, g_sum_out=out, workspace=ws, sq_out=sq)),
+         lambda: sbp.grad_sq_norm(peers, None, 0.125, n, g_sum_out=out, workspace=ws, sq_out=sq),
+         (8, 0, 0, 1, 0), peers, [], out, None),
         ("accumulate, R=8, first", 8, 1, 20,
-         lambda: sbp.accumulate_grads(acc, peers, first=True)),
+         lambda: sbp.accumulate_grads(acc, peers, first=True),
+         (8, 0, 0, 1, 0), peers, [], acc, None),
         ("accumulate, R=8, later", 9, 1, 24,
-         lambda: sbp.accumulate_grads(acc, peers, first=False)),
-        ("fused step from G (R=0)", 4, 4, 30, fused(0, True)),
-        ("fused step, R=2", 5, 4, 30, fused(2, False)),
-        ("fused step, R=8 (the headline)", 11, 4, 42, fused(8, False)),
-        ("fused step, R=8 + accumulator", 12, 4, 46, fused(8, True)),
+         lambda: sbp.accumulate_grads(acc, peers, first=False),
+         (8, 1, 1, 0, 0), peers, [acc], None, None),
+        ("fused step from G (R=0)", 4, 4, 30, fused(0, True),
+         (0, 4, 3, 0, 1), [], [master, m, v, acc], None, p),
+        ("fused step, R=2", 5, 4, 30, fused(2, False),
+         (2, 3, 3, 0, 1), peers[:2], [master, m, v], None, p),
+        ("fused step, R=8 (the headline)", 11, 4, 42, fused(8, False),
+         (8, 3, 3, 0, 1), peers, [master, m, v], None, p),
+        ("fused step, R=8 + accumulator", 12, 4, 46, fused(8, True),
+         (8, 4, 3, 0, 1), peers, [master, m, v, acc], None, p),
     ]
-    times = {k[0]: [] for k in kinds}
+    # every configuration to time: the kernels, then each kernel's probes
+    calls = {}
+    for name, _, _, bpe, f, shape, b, fa, g, o in kinds:
+        calls[name] = (f, n, bpe, None)
+        lane = 16 * shape[0] + 32 * shape[1]
+        for gpl in ((1, 2, 4) if lane <= 32 else (1, 2)):
+            for bpc in (1, 2, 3, 4, 0):
+                for C in (32, 64):
+                    call, cover = probe(shape, b, fa, g, o, gpl, bpc, C)
+                    calls[(name, gpl, bpc, C)] = (call, cover, bpe, (gpl, bpc, C))
+    times = {k: [] for k in calls}
     torch.cuda.synchronize()
     for ps in range(passes):
-        for name, _, _, _, f in kinds:
+        for key, (f, _, _, _) in calls.items():
             for _ in range(2):
                 f()
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(reps)]
             for a, b in evs:
-                a.record()
+                a.record(stream)
                 f()
-                b.record()
+                b.record(stream)
             torch.cuda.synchronize()
-            times[name] += [a.elapsed_time(b) for a, b in evs]
+            times[key] += [a.elapsed_time(b) for a, b in evs]
         log(f"stream mix: pass {ps + 1} of {passes} done")
+
+    def rate(key):
+        _, cover, bpe, _ = calls[key]
+        return bpe * cover / (st.median(times[key]) * 1e-3) / 1e9
+
     rows = []
-    for name, rd, wr, bpe, _ in kinds:
+    for name, rd, wr, bpe, _, shape, _, _, _, _ in kinds:
         ms = st.median(times[name])
-        gbs = bpe * n / (ms * 1e-3) / 1e9
+        gbs = rate(name)
+        best = max((k for k in calls if isinstance(k, tuple) and k[0] == name), key=rate)
+        pg = rate(best)
+        gpl, bpc, C = calls[best][3]
         rows.append({"kind": name, "read_streams": rd, "write_streams": wr,
-                     "bytes_per_elem": bpe, "ms_median": ms, "gbs": gbs, "frac": gbs / PEAK_GBS})
-        log(f"stream mix: {name:34s} {rd:2d}R+{wr}W {bpe:2d} B {ms:.3f} ms {gbs:.0f} GB/s "
-            f"{100 * gbs / PEAK_GBS:.1f}%")
+                     "bytes_per_elem": bpe, "ms_median": ms, "gbs": gbs, "frac": gbs / PEAK_GBS,
+                     "probe_shape": list(shape),
+                     "probe_best": {"gbs": pg, "frac": pg / PEAK_GBS, "groups_per_lane": gpl,
+                                    "blocks_per_cu": bpc, "xcd_chunk": C},
+                     "frac_of_probe": gbs / pg})
+        log(f"stream mix: {name:38s} {rd:2d}R+{wr}W {bpe:2d} B {ms:.3f} ms {gbs:.0f} GB/s "
+            f"{100 * gbs / PEAK_GBS:.1f}%; its mix's probe {pg:.0f} GB/s "
+            f"(gpl {gpl}, {bpc or 'no cap'} blocks/CU, C={C}): {gbs / pg:.3f}")
     return {"stream_mix": rows, "n": n, "passes": passes, "reps": reps}
 
 

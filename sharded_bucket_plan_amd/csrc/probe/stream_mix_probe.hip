@@ -27,6 +27,11 @@
 //   7  as 1, and the loads too go through LDS: wave w loads whole streams of
 //      the tile (peers 2w and 2w+1, and master / m / v for w < 3); R = 8 only
 // Only whole tiles are covered.
+//
+// sbp_probe_streams moves the traffic of each of the library's other
+// streaming kernels the same way (reduce, accumulate, the squared-norm
+// pass, the pack's copy, the fused step from G or with an accumulator), so
+// each kernel's rate can be read against the ceiling of its own mix.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -221,6 +226,69 @@ __global__ void __launch_bounds__(256) copy_probe(const u32x4* __restrict__ a,
   for (int j = 0; j < 4; ++j) b[base + j * 256] = x[j];
 }
 
+// ---- the traffic of any of the library's streaming kernels ------------------
+// RB bf16 read streams, RF fp32 read streams of which the first WF are
+// written back in place, WG fp32 write-only streams (0 or 1), WB bf16
+// write-only streams (0 or 1).  GPL groups of 8 consecutive elements per
+// lane, the groups of a lane 256 apart (tile = 2048 * GPL elements); every
+// load of a lane before its stores.  Every store depends on every load of its
+// group; with mask = 0 in-place streams are written back unchanged and the
+// write-only streams get zeros.
+struct StreamArrays {
+  const u32x4* b[8];
+  u32x4* f[4];
+  u32x4* g;
+  u32x4* o;
+  uint32_t* sink;
+};
+
+template <int RB, int RF, int WF, int WG, int WB, int GPL>
+__global__ void __launch_bounds__(256) streams_probe(StreamArrays A, uint32_t mask, unsigned C) {
+  static_assert(WF <= RF && RB <= 8 && RF <= 4, "stream counts");
+  const int64_t g0 = (int64_t)dealt_tile(C) * 256 * GPL + threadIdx.x;
+  u32x4 x[GPL];
+  u32x4 F[GPL][RF > 0 ? RF : 1][2];
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int64_t gi = g0 + j * 256;
+    x[j] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < RB; ++r) x[j] ^= A.b[r][gi];
+#pragma unroll
+    for (int q = 0; q < RF; ++q) {
+      F[j][q][0] = A.f[q][2 * gi];
+      F[j][q][1] = A.f[q][2 * gi + 1];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+#pragma unroll
+    for (int q = WF; q < RF; ++q) x[j] ^= F[j][q][0] ^ F[j][q][1];
+  }
+  if constexpr (WF + WG + WB == 0) {
+    u32x4 y = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) y ^= x[j];
+    if ((y.x ^ y.y ^ y.z ^ y.w) == (0x9E3779B9u | ~mask)) A.sink[0] = y.x;  // never with mask 0
+  } else {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int64_t gi = g0 + j * 256;
+      const u32x4 y = x[j] & mask;
+#pragma unroll
+      for (int q = 0; q < WF; ++q) {
+        A.f[q][2 * gi] = F[j][q][0] ^ y;
+        A.f[q][2 * gi + 1] = F[j][q][1] ^ y;
+      }
+      if constexpr (WG) {
+        A.g[2 * gi] = y;
+        A.g[2 * gi + 1] = y;
+      }
+      if constexpr (WB) A.o[gi] = y;
+    }
+  }
+}
+
 constexpr unsigned kLdsNeed[8] = {0, 1792 * 16, 0, 0, 0, 0, 0, 3584 * 16};
 
 int lds_cap(int blocks_per_cu, unsigned need, unsigned* out) {
@@ -261,9 +329,69 @@ int launch_r(int variant, const Arrays& A, unsigned tiles, uint32_t mask, unsign
   }
 }
 
+// The shapes (RB, RF, WF, WG, WB) of the library's kernels: the squared-norm
+// pass at R = 1, 2, 8, of the accumulator, and at R = 8 with it; the pack
+// (a bf16 copy); reduce at R = 1 and R = 8 (also the norm pass writing G and
+// the first accumulate); the later accumulate; the fused step from G, at
+// R = 2, at R = 8 and at R = 8 with the accumulator.
+#define SBP_PROBE_SHAPES(X) \
+  X(1, 0, 0, 0, 0) X(2, 0, 0, 0, 0) X(0, 1, 0, 0, 0) X(8, 0, 0, 0, 0) X(8, 1, 0, 0, 0) \
+  X(1, 0, 0, 0, 1) X(1, 0, 0, 1, 0) X(8, 0, 0, 1, 0) X(8, 1, 1, 0, 0) X(0, 4, 3, 0, 1) \
+  X(2, 3, 3, 0, 1) X(8, 3, 3, 0, 1) X(8, 4, 3, 0, 1)
+
+int launch_streams(const int* sh, int gpl, const StreamArrays& A, unsigned grid, uint32_t mask,
+                   unsigned lds, unsigned C, hipStream_t stream) {
+#define SBP_PROBE_TRY(rb, rf, wf, wg, wb)                                                  \
+  if (sh[0] == rb && sh[1] == rf && sh[2] == wf && sh[3] == wg && sh[4] == wb) {           \
+    if (gpl == 1) return go(streams_probe<rb, rf, wf, wg, wb, 1>, grid, lds, stream, A, mask, C); \
+    if (gpl == 2) return go(streams_probe<rb, rf, wf, wg, wb, 2>, grid, lds, stream, A, mask, C); \
+    if (gpl == 4) return go(streams_probe<rb, rf, wf, wg, wb, 4>, grid, lds, stream, A, mask, C); \
+    return -1;                                                                             \
+  }
+  SBP_PROBE_SHAPES(SBP_PROBE_TRY)
+#undef SBP_PROBE_TRY
+  return -1;
+}
+
 }  // namespace
 
 extern "C" {
+
+// One zero-arithmetic pass of shape sh = {RB, RF, WF, WG, WB} (one of the
+// shapes listed above) over n_tiles whole tiles of 2048 * gpl elements (gpl
+// 1, 2 or 4).  b: host array of RB device pointers to bf16 arrays; f: host
+// array of RF device pointers to fp32 arrays (the first WF written back in
+// place); g: fp32 array (WG = 1) or null; o: bf16 array (WB = 1) or null;
+// sink: one device uint32 (read-only shapes).  Every array 16-byte aligned
+// and at least n_tiles * 2048 * gpl elements; the written ones disjoint from
+// the others.  blocks_per_cu: 0 = no cap.  Returns 0, or -1 on a bad
+// argument or a launch failure.
+int sbp_probe_streams(const int* sh, int gpl, const void* const* b, void* const* f, void* g,
+                      void* o, void* sink, int64_t n_tiles, uint32_t mask, int blocks_per_cu,
+                      unsigned xcd_chunk, hipStream_t stream) {
+  if (sh == nullptr || sh[0] < 0 || sh[0] > 8 || sh[1] < 0 || sh[1] > 4 || sh[2] < 0 ||
+      sh[2] > sh[1] || sh[3] < 0 || sh[3] > 1 || sh[4] < 0 || sh[4] > 1 ||
+      (gpl != 1 && gpl != 2 && gpl != 4) || n_tiles < 1 || n_tiles > (int64_t{1} << 24) - 1 ||
+      sink == nullptr || blocks_per_cu < 0 || blocks_per_cu > 8 ||
+      (sh[0] > 0 && b == nullptr) || (sh[1] > 0 && f == nullptr) ||
+      (sh[3] && g == nullptr) || (sh[4] && o == nullptr))
+    return -1;
+  StreamArrays A{};
+  for (int r = 0; r < sh[0]; ++r) {
+    if (b[r] == nullptr) return -1;
+    A.b[r] = static_cast<const u32x4*>(b[r]);
+  }
+  for (int q = 0; q < sh[1]; ++q) {
+    if (f[q] == nullptr) return -1;
+    A.f[q] = static_cast<u32x4*>(f[q]);
+  }
+  A.g = static_cast<u32x4*>(g);
+  A.o = static_cast<u32x4*>(o);
+  A.sink = static_cast<uint32_t*>(sink);
+  unsigned lds = 0;
+  if (lds_cap(blocks_per_cu, 0, &lds)) return -1;
+  return launch_streams(sh, gpl, A, static_cast<unsigned>(n_tiles), mask, lds, xcd_chunk, stream);
+}
 
 // One probe pass over n_tiles whole 2048-element tiles (variants 5 and 6
 // cover the whole 4096-element tiles inside them).  peers: host array of R
