@@ -409,10 +409,15 @@ sbp_status sbp_adamw_shard_grouped(const void* const* peers, int32_t R,
  * sbp_grad_sq_norm: this rank's squared norm of the normalised gradient,
  *   sum_i (double) g_i^2 with g_i = fl(G_i * scale), G as in sbp_adamw_shard
  *   (G = acc + S, S, or acc when R == 0), accumulated in float64 (each square
- *   is exact) in a fixed order: one partial per 2048-element tile in
- *   `workspace`, then a tree of fixed shape over those partials (groups of
- *   2048 consecutive partials, level by level, the levels also kept in
- *   `workspace`) into *sq_out (device).
+ *   is exact) in a fixed order: one partial per tile of 2048 * gpl elements
+ *   in `workspace` (gpl = 4 when a group of 8 elements loads 16 bytes: R = 1
+ *   without acc; 2 when it loads 32: R = 2 without acc, or acc alone; else
+ *   1), then a tree of fixed shape over those partials (groups of 2048
+ *   consecutive partials, level by level, the levels also kept in
+ *   `workspace`) into *sq_out (device).  Within a tile, each of the 256
+ *   lanes adds its 8 * gpl squares in element order (its groups 256 groups
+ *   apart; in the first tile lane l then adds tail element 8 * (n / 8) + l,
+ *   if any), and the lanes' sums meet in a fixed tree.
  *   Results are deterministic run to run.  If g_sum_out is given, G (fp32,
  *   unscaled) is also written there, so the update can follow as
  *   sbp_adamw_shard(R = 0, acc = g_sum_out, scale = clipped scale) without
