@@ -405,7 +405,7 @@ def summarize_sweep_pmc(pmc_dir, sweep_json, rates_json, command):
     counters = sorted({c for ctr in last.values() for c in ctr})
     labels = list(dict.fromkeys(label for (_, label) in last))
     sets = sw["phase_a_sets"]
-    lines = ["Command (repository root R on the GPU box, TMPDIR=/tmp, cwd /tmp):", "",
+    lines = ["Command (repository root R on the measuring machine, TMPDIR=/tmp, cwd /tmp):", "",
              "```", command, "```", "",
              f"Box: {sw.get('box')}" + (f"; rates from a separate `--placement-sweep` run on "
                                         f"box {rates.get('box')}" if rates else ""), ""]
@@ -696,7 +696,7 @@ def _oracle_core_worker(workload_name, seed, k, target_s, chunk, ready, go, resu
 
 def host_cores():
     """Host cores this process may use: the affinity mask, capped by
-    OMP_NUM_THREADS where that is set (a GPU machine's share of its host)."""
+    OMP_NUM_THREADS where that is set (this process's share of a shared host)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit() and int(env) > 0:

@@ -81,7 +81,7 @@ def assert_bits_equal(got, want, what):
 
 
 def assert_state_close(got, want, what, f32_ulps=4, bf16_ulps=1):
-    """spec bar: master/m/v within 4 fp32 ulp, params within 1 bf16 ulp.
+    """Tolerance for the state: master/m/v within 4 fp32 ulp, params within 1 bf16 ulp.
     Returns the largest distance seen (expected 0: the path is bit-exact)."""
     th, m, v, p = got
     wth, wm, wv, wp = want

@@ -216,7 +216,8 @@ def clipped_digests(job):
 
 def workers():
     """Worker processes for this host: the cores this process may use,
-    capped by OMP_NUM_THREADS where set (a GPU machine's share) and at 16."""
+    capped by OMP_NUM_THREADS where set (this process's share of a shared host)
+    and at 16."""
     n = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS", "")
     if env.isdigit() and int(env) > 0:
