@@ -163,11 +163,16 @@ def _elem_groups(starts, groups, n):
     return g
 
 
-@pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 8] for n in SIZES] + [(8, BIG)])
-def test_adamw_shard_grouped(R, n):
-    """Per-group lr and weight decay from a run table, every element."""
+@pytest.mark.parametrize("R,n,with_acc",
+                         [(R, n, R == 0) for R in [0, 1, 2, 8] for n in SIZES]
+                         + [(R, n, True) for R in [3, 8] for n in SIZES]
+                         + [(8, BIG, False), (8, BIG, True)])
+def test_adamw_shard_grouped(R, n, with_acc):
+    """Per-group lr and weight decay from a run table, every element: the
+    peers alone, an accumulator of an earlier microbatch alone (R = 0), or
+    both."""
     import torch
-    rng = np.random.default_rng(n * 31 + R)
+    rng = np.random.default_rng(n * 31 + R + (7 if with_acc else 0))
     starts, groups = _random_runs(n, rng)
     eg = _elem_groups(starts, groups, n)
     rs, rg = torch.from_numpy(starts).to(H.dev()), torch.from_numpy(groups).to(H.dev())
@@ -175,15 +180,15 @@ def test_adamw_shard_grouped(R, n):
     gs = [H.guarded_from(x) for x in (th, m, v)]
     dth, dm, dv = (x[1] for x in gs)
     pw, dp, g = H.guarded(n, 2)
-    acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if R == 0 else None
+    acc_d = torch.empty(n, dtype=torch.float32, device=H.dev()) if with_acc else None
     want = (th, m, v, None)
     bufs = None
     for t in (1, 2):
         acc_h = None
-        if R == 0:
+        if with_acc:
             sbp.accumulate_grads(acc_d, H.dev_peers(16, t, 0, 3, n, 1e-3), first=True)
             acc_h = OS.reduce_peers(H.host_peers(16, t, 0, 3, n, 1e-3))
-        else:
+        if R:
             bufs = H.dev_peers(16, t, 1, R, n, 1e-3, bufs)
         scale = sbp.mean_scale(max(R, 3))
         sbp.adamw_shard_grouped(bufs or [], acc_d, scale, dth, dm, dv, dp, HP, t, GROUPS, rs, rg)
@@ -193,7 +198,7 @@ def test_adamw_shard_grouped(R, n):
     torch.cuda.synchronize()
     got = (H.to_np_f32(dth), H.to_np_f32(dm), H.to_np_f32(dv), H.to_np_u16(dp))
     for a, b, name in zip(got, want, ("master", "m", "v", "param")):
-        H.assert_bits_equal(a, b, f"grouped R={R} n={n} {name}")
+        H.assert_bits_equal(a, b, f"grouped R={R} n={n} acc={with_acc} {name}")
     assert H.canaries_intact(pw, g)
     assert all(H.canaries_intact(w, gg) for w, _, gg in gs)
 
