@@ -18,6 +18,9 @@ HP = sbp.AdamW()
 SIZES = [1, 7, 8, 9, 2047, 256 * 8 * 3 + 5]
 # 16.8M elements make one grid-stride pass of the largest grid; this spans 2+
 BIG = 256 * 32 * 256 * 8 * 2 + 13
+# sizes whose tile grids end in a partial round of the XCD deal: 301 and 522
+# tiles of 2048 (one full round of 8 chunks of 32 tiles, or of 64, then a rest)
+ROUNDS = [300 * 2048 + 5, 521 * 2048 + 3]
 
 
 @pytest.fixture(autouse=True)
@@ -43,7 +46,7 @@ def test_device_generator_matches_host():
 
 
 @pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
-@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("n", SIZES + ROUNDS)
 def test_reduce_shard(R, n):
     import torch
     peers = H.dev_peers(11, 1, 0, R, n, 1e-3)
@@ -68,7 +71,7 @@ def test_reduce_shard_big_multi_pass():
 
 
 @pytest.mark.parametrize("R", [1, 3, 8])
-@pytest.mark.parametrize("n", [1, 9, 256 * 8 * 3 + 5, BIG])
+@pytest.mark.parametrize("n", [1, 9, 256 * 8 * 3 + 5, BIG] + ROUNDS)
 def test_accumulate_grads(R, n):
     import torch
     K = 3
@@ -90,7 +93,8 @@ def _state(seed, n):
 
 
 # every peer count at the small sizes; the multi-pass size at R = 8
-@pytest.mark.parametrize("R,n", [(R, n) for R in [1, 2, 4, 7, 8, 16] for n in SIZES] + [(8, BIG)])
+@pytest.mark.parametrize("R,n", [(R, n) for R in [1, 2, 4, 7, 8, 16] for n in SIZES] + [(8, BIG)]
+                         + [(R, n) for R in [2, 8] for n in ROUNDS])
 @pytest.mark.parametrize("with_acc", [False, True])
 def test_adamw_shard(R, n, with_acc):
     import torch
@@ -166,7 +170,8 @@ def _elem_groups(starts, groups, n):
 @pytest.mark.parametrize("R,n,with_acc",
                          [(R, n, R == 0) for R in [0, 1, 2, 8] for n in SIZES]
                          + [(R, n, True) for R in [3, 8] for n in SIZES]
-                         + [(8, BIG, False), (8, BIG, True)])
+                         + [(8, BIG, False), (8, BIG, True)]
+                         + [(8, n, a) for n in ROUNDS for a in (False, True)])
 def test_adamw_shard_grouped(R, n, with_acc):
     """Per-group lr and weight decay from a run table, every element: the
     peers alone, an accumulator of an earlier microbatch alone (R = 0), or
@@ -566,7 +571,8 @@ def test_layout_segment_longer_than_2_30():
 # R = 1 and R = 2 without an accumulator, and R = 0, take 4 / 2 / 2 groups per lane
 @pytest.mark.parametrize("R,n", [(R, n) for R in [0, 1, 2, 3, 8]
                                   for n in [1, 9, 2047, 256 * 8 * 3 + 5, 256 * 8 * 9 + 3]]
-                         + [(8, BIG), (1, BIG), (2, BIG), (0, BIG)])
+                         + [(8, BIG), (1, BIG), (2, BIG), (0, BIG)]
+                         + [(R, n) for R in [3, 8] for n in ROUNDS])
 @pytest.mark.parametrize("write", [False, True])
 def test_grad_sq_norm(R, n, write):
     import torch
